@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs shared by the GPU tests, the benchmark and the oracle checks.
+
+This module only draws numbers and builds the caller-side RoPE angle table; it holds none of
+the attention, normalisation or cache arithmetic, and it imports neither the GPU library nor
+the oracle.
+
+Recipe (the pages' workloads use trained video models whose weights and data are not
+available, so every tensor here is a stand-in of the same shape and dtype):
+  * a fresh ``torch.Generator`` seeded per tensor set; fp32 N(0, 1) draws in the order
+    q, k, v (then gamma_q, gamma_k), each cast round-to-nearest-even to the I/O dtype;
+  * RMSNorm weights: bf16(1 + 0.1 * N(0, 1)), held as fp32 (the learned weights are unknown);
+  * RoPE angles: theta_{p,r} = p * base^(-2r/d) computed in fp64 from absolute stream positions
+    p and stored as fp32 [L, d/2] -- the expanded per-position angle table that the page
+    "flashdreams.accelerated" (section "Multi Head Attention Definition") says the attention
+    module receives from its caller.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def normal(shape, dtype: str, gen: torch.Generator, scale: float = 1.0) -> torch.Tensor:
+    """fp32 N(0, 1) * scale, cast to the 16-bit dtype (CPU tensor)."""
+    x = torch.randn(tuple(shape), generator=gen, dtype=torch.float32)
+    if scale != 1.0:
+        x = x * scale
+    return x.to(DTYPES[dtype])
+
+
+def attention_inputs(B: int, Lq: int, Lk: int, Hq: int, Hkv: int, d: int, dtype: str, seed: int,
+                     q_scale: float = 1.0):
+    """q [B, Lq, Hq, d], k and v [B, Lk, Hkv, d], drawn in that order from one generator."""
+    g = torch.Generator().manual_seed(seed)
+    q = normal((B, Lq, Hq, d), dtype, g, q_scale)
+    k = normal((B, Lk, Hkv, d), dtype, g)
+    v = normal((B, Lk, Hkv, d), dtype, g)
+    return q, k, v
+
+
+def norm_weight(d: int, gen: torch.Generator) -> torch.Tensor:
+    """Synthetic RMSNorm weight: bf16(1 + 0.1 N(0,1)) values held in fp32 [d]."""
+    w = 1.0 + 0.1 * torch.randn((d,), generator=gen, dtype=torch.float32)
+    return w.to(torch.bfloat16).to(torch.float32)
+
+
+def rope_angles(positions, d: int, base: float = 10000.0) -> torch.Tensor:
+    """fp32 [len(positions), d/2] table of p * base^(-2r/d), computed in fp64."""
+    p = np.asarray(positions, dtype=np.float64)[:, None]
+    r = np.arange(d // 2, dtype=np.float64)[None, :]
+    ang = p * np.power(float(base), -2.0 * r / d)
+    return torch.from_numpy(ang.astype(np.float32))
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of a CPU bf16/f16 tensor as a uint16 numpy array."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One benchmark configuration (shapes and dtypes of the pages' workloads)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    seed: int
+    prologue: str = "none"   # "none" | "qk_norm_rope" (streaming self-attention) | "q_norm" (cross)
+    chunk: int = 0           # streaming: chunk length (= Lq)
+    window: int = 0          # streaming: cache capacity in tokens (sink 0)
+
+    @property
+    def flops(self) -> float:
+        """Attention flop count 4 * B * H * Lq * Lk * d (the metric's formula)."""
+        return 4.0 * self.B * self.Hq * self.Lq * self.Lk * self.d
+
+
+WORKLOADS = {
+    # non-causal MHA, [1, 257, 8, 128] bf16, scale 1/sqrt(128)
+    "mha_257_bf16": Workload("mha_257_bf16", 1, 8, 8, 257, 257, 128, "bf16", False, 128 ** -0.5, 1001),
+    # causal MHA, [2, 2048, 8, 64] fp16, scale 1/8
+    "causal_2048_f16": Workload("causal_2048_f16", 2, 8, 8, 2048, 2048, 64, "f16", True, 0.125, 1002),
+    # streaming self-attention: 40 heads, d 128, chunk 1785, rolling cache of 4 chunks (7140 keys)
+    "stream_self_1785x4": Workload("stream_self_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
+                                   128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140),
+    # cross-attention over a static 512-token context, B = 2 (guidance pair), Q RMSNorm only
+    "cross_1785x512": Workload("cross_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
+                               128 ** -0.5, 1004, "q_norm"),
+    # long non-causal MHA, [1, 20480, 56, 128] bf16
+    "mha_20480_bf16": Workload("mha_20480_bf16", 1, 56, 56, 20480, 20480, 128, "bf16", False,
+                               128 ** -0.5, 1005),
+}

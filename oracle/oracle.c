@@ -1,0 +1,194 @@
+/*
+ * Reference oracle for streaming multi-head attention: plain, slow, fp64, CPU only.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load this library. The GPU product path never calls it, links it or shares code
+ * with it: the two are independent implementations of the same definitions.
+ *
+ * Every function restates a definition from the page "flashdreams.accelerated" (developer
+ * guide), section "Multi Head Attention Definition":
+ *   - 16-bit float decoding is the IEEE-754 binary16 / bfloat16 bit-format definition;
+ *   - RMSNorm: gamma (.) z / sqrt(mean(z^2) + eps), the RMSNorm equation of that section;
+ *   - RoPE: the 2x2 rotation of pair r by angle theta_{p,r} (rotation equation), with the
+ *     split-half pairs (r, r + d/2) or interleaved pairs (2r, 2r + 1) named there;
+ *   - attention: A_h = softmax(Q_h K_h^T * scale) V_h, the scaled dot-product equation, one
+ *     query row at a time, over the full key range (no tiling, no online rescaling).
+ * Subtracting the row maximum before exp() is the textbook identity
+ * softmax(s) = softmax(s - c); it changes no value in exact arithmetic.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread oracle.c -lm
+ * (no fused multiply-add contraction, so each expression rounds as written).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- 16-bit float decoding */
+
+/* bfloat16: the upper 16 bits of an IEEE-754 binary32 value. */
+static double decode_bf16_one(uint16_t h) {
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double decode_f16_one(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24); /* subnormal: frac * 2^-14 * 2^-10 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/1024) * 2^(expo-15) */
+    return sign ? -mag : mag;
+}
+
+void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_bf16_one(in[i]);
+}
+
+void oracle_decode_f16(const uint16_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_f16_one(in[i]);
+}
+
+/* ---------------------------------------------------------------- RMSNorm */
+
+/* rows x m matrix z, one RMSNorm per row: out = gamma * z / sqrt((1/m) sum z^2 + eps).
+ * Head scope is m = d over rows (b, token, head); inner scope is m = H*d over rows (b, token). */
+void oracle_rmsnorm(const double* z, const double* gamma, double* out, int64_t rows, int m, double eps) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* zr = z + r * m;
+        double* o = out + r * m;
+        double ss = 0.0;
+        for (int t = 0; t < m; ++t) ss += zr[t] * zr[t];
+        double denom = sqrt(ss / (double)m + eps);
+        for (int t = 0; t < m; ++t) o[t] = gamma[t] * (zr[t] / denom);
+    }
+}
+
+/* ---------------------------------------------------------------- RoPE */
+
+/* z, out: [B, L, H, d]; angles: [L, d/2] (angle of pair r at position p is angles[p*(d/2) + r]).
+ * style 1 = split-half pairs (r, r + d/2); style 2 = interleaved pairs (2r, 2r + 1).
+ * Rotation: a' = cos*a - sin*b ; b' = sin*a + cos*b. */
+void oracle_rope(const double* z, const double* angles, double* out, int B, int L, int H, int d, int style) {
+    int half = d / 2;
+    for (int b = 0; b < B; ++b)
+        for (int p = 0; p < L; ++p)
+            for (int h = 0; h < H; ++h) {
+                int64_t base = (((int64_t)b * L + p) * H + h) * d;
+                const double* zr = z + base;
+                double* o = out + base;
+                for (int r = 0; r < half; ++r) {
+                    int ia = (style == 1) ? r : 2 * r;
+                    int ib = (style == 1) ? r + half : 2 * r + 1;
+                    double th = angles[(int64_t)p * half + r];
+                    double c = cos(th), s = sin(th);
+                    double a = zr[ia], bb = zr[ib];
+                    o[ia] = c * a - s * bb;
+                    o[ib] = s * a + c * bb;
+                }
+            }
+}
+
+/* ---------------------------------------------------------------- attention */
+
+typedef struct {
+    const double *q, *k, *v;
+    double* out;
+    const int64_t* rows; /* flat indices into [B, Lq, Hq]; NULL = all rows in order */
+    int64_t nrows;
+    int B, Hq, Hkv, Lq, Lk, d, causal;
+    double scale;
+    int tid, nthreads;
+} attn_job;
+
+/* One query row: s_j = scale * <q_i, k_j> for every visible key j, then
+ * o = sum_j softmax(s)_j v_j. Causal visibility: key j is visible to query i when
+ * j <= i + (Lk - Lq) (the query block sits at the end of the key sequence). */
+static void attention_row(const attn_job* J, int64_t row, double* scores, double* o) {
+    int64_t h = row % J->Hq;
+    int64_t i = (row / J->Hq) % J->Lq;
+    int64_t b = row / ((int64_t)J->Hq * J->Lq);
+    int group = J->Hq / J->Hkv;
+    int64_t hk = h / group;
+    int d = J->d;
+    const double* qi = J->q + row * d;
+    int64_t nvis = J->Lk;
+    if (J->causal) {
+        int64_t last = i + (J->Lk - J->Lq);
+        nvis = last + 1 < J->Lk ? last + 1 : J->Lk;
+        if (nvis < 0) nvis = 0;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double* kj = J->k + (((int64_t)b * J->Lk + j) * J->Hkv + hk) * d;
+        double dot = 0.0;
+        for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+        scores[j] = J->scale * dot;
+        if (scores[j] > m) m = scores[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        scores[j] = exp(scores[j] - m);
+        l += scores[j];
+    }
+    for (int t = 0; t < d; ++t) o[t] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double* vj = J->v + (((int64_t)b * J->Lk + j) * J->Hkv + hk) * d;
+        for (int t = 0; t < d; ++t) o[t] += scores[j] * vj[t];
+    }
+    for (int t = 0; t < d; ++t) o[t] = o[t] / l;
+}
+
+static void* attention_worker(void* arg) {
+    attn_job* J = (attn_job*)arg;
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(J->Lk > 0 ? J->Lk : 1));
+    if (!scores) return (void*)1;
+    for (int64_t n = J->tid; n < J->nrows; n += J->nthreads) {
+        int64_t row = J->rows ? J->rows[n] : n;
+        attention_row(J, row, scores, J->out + n * J->d);
+    }
+    free(scores);
+    return NULL;
+}
+
+/* q: [B, Lq, Hq, d], k and v: [B, Lk, Hkv, d], contiguous fp64. Query head h reads key/value
+ * head h / (Hq / Hkv). out: [nrows, d], row n is the attention output of query row rows[n]
+ * (flat index (b * Lq + i) * Hq + h), or of row n when rows is NULL (then nrows = B*Lq*Hq).
+ * Returns 0 on success, -1 on invalid arguments or allocation failure. */
+int oracle_attention(const double* q, const double* k, const double* v, double* out,
+                     const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                     double scale, int causal, int nthreads) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq < 0 || Lk < 0 || d <= 0) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    attn_job jobs[256];
+    pthread_t th[256];
+    int created[256];
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, causal, scale, t, nthreads};
+        jobs[t] = J;
+        created[t] = 0;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        created[t] = pthread_create(&th[t], NULL, attention_worker, &jobs[t]) == 0;
+    if (attention_worker(&jobs[0]) != NULL) rc = -1;
+    for (int t = 1; t < nthreads; ++t) {
+        void* r = NULL;
+        if (created[t])
+            pthread_join(th[t], &r);
+        else
+            r = attention_worker(&jobs[t]); /* could not start a thread: do its rows here */
+        if (r != NULL) rc = -1;
+    }
+    return rc;
+}

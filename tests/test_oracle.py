@@ -1,0 +1,317 @@
+"""Pins for the fp64 oracle: closed forms, invariants, brute force and library cross-checks.
+
+Every check here ties the oracle to something other than itself -- a value worked out by hand
+from the definitions on the page "flashdreams.accelerated" (section "Multi Head Attention
+Definition"), an algebraic invariant of those definitions, or an independent library routine
+(PyTorch float64 SDPA / rms_norm, numpy's binary16 conversion). No check re-types the oracle's
+own formula.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_attention_streaming_amd import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(*shape, scale=1.0):
+    return RNG.standard_normal(shape) * scale
+
+
+def _sdpa64(q, k, v, scale, causal=False, mask=None):
+    """PyTorch CPU float64 SDPA on [B, L, H, d] arrays (library cross-check)."""
+    tq = torch.from_numpy(np.ascontiguousarray(q)).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.ascontiguousarray(k)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 2, 1, 3)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, is_causal=causal,
+                                                         scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+# ------------------------------------------------------------------ 16-bit formats
+
+def test_decode_matches_library_for_every_pattern():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = oracle.decode(pats, "f16")
+    ref16 = pats.view(np.float16).astype(np.float64)
+    same = (f16 == ref16) | (np.isnan(f16) & np.isnan(ref16))
+    assert same.all()
+    bf = oracle.decode(pats, "bf16")
+    refbf = torch.from_numpy(pats.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (bf == refbf) | (np.isnan(bf) & np.isnan(refbf))
+    assert same.all()
+
+
+def test_decode_known_values():
+    pats = np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x3C00], dtype=np.uint16)
+    assert list(oracle.decode(pats[:4], "bf16")) == [1.0, -2.0, math.inf, 2.0 ** -133]
+    f = oracle.decode(np.array([0x3C00, 0x7BFF, 0x0001, 0x3555, 0xC400], dtype=np.uint16), "f16")
+    assert list(f) == [1.0, 65504.0, 2.0 ** -24, 0.333251953125, -4.0]
+
+
+def test_round_to_bf16_hand_cases():
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8 + 2 ** -30),
+                  2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 0.0, -0.0, 3.0e38, 3.5e38])
+    r = oracle.round_to(x, "bf16")
+    # tie to even (down), tie to even (up), just above a tie (direct rounding, no fp32 detour),
+    # smallest subnormal, half of it (tie to even 0), 1.5x half (rounds up), zeros, large, overflow
+    expect = [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -7), 2.0 ** -133, 0.0, 2.0 ** -133, 0.0, -0.0,
+              float(torch.tensor(3.0e38).to(torch.bfloat16).double()), math.inf]
+    assert list(r) == expect
+    assert math.copysign(1.0, r[8]) == -1.0
+
+
+def test_round_to_matches_libraries():
+    # fp32-representable inputs: torch's float32 -> bfloat16 conversion is round-to-nearest-even
+    x32 = (RNG.standard_normal(200000) * np.exp(RNG.uniform(-30, 30, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_to(x32.astype(np.float64), "bf16"), ref)
+    # numpy converts float64 -> float16 directly with round-to-nearest-even
+    x64 = RNG.standard_normal(200000) * np.exp(RNG.uniform(-12, 9, 200000))
+    ref16 = x64.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.round_to(x64, "f16"), ref16)
+
+
+# ------------------------------------------------------------------ attention
+
+@pytest.mark.parametrize("case", _load("attention_two_keys.json")["cases"], ids=lambda c: c["name"])
+def test_attention_hand_worked_two_key_cases(case):
+    q, k, v = (np.array(case[n], dtype=np.float64) for n in ("q", "k", "v"))
+    out = oracle.attention(q, k, v, case["scale"], case["causal"])
+    np.testing.assert_allclose(out, np.array(case["expected"]), rtol=0, atol=1e-12)
+
+
+def test_attention_single_key_returns_v():
+    q, k, v = _rand(2, 5, 3, 16), _rand(2, 1, 3, 16), _rand(2, 1, 3, 16)
+    out = oracle.attention(q, k, v, 0.25)
+    np.testing.assert_allclose(out, np.broadcast_to(v, out.shape), rtol=0, atol=1e-14)
+
+
+def test_attention_zero_query_returns_mean_of_v():
+    q, k, v = np.zeros((1, 4, 2, 8)), _rand(1, 37, 2, 8), _rand(1, 37, 2, 8)
+    out = oracle.attention(q, k, v, 0.3)
+    mean = v.mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(out, np.broadcast_to(mean, out.shape), rtol=0, atol=1e-14)
+
+
+def test_attention_causal_first_row_returns_v0():
+    q, k, v = _rand(2, 9, 3, 8), _rand(2, 9, 3, 8), _rand(2, 9, 3, 8)
+    out = oracle.attention(q, k, v, 0.5, causal=True)
+    np.testing.assert_allclose(out[:, 0], v[:, 0], rtol=0, atol=1e-14)
+
+
+def test_attention_brute_force_two_heads_sigmoid():
+    # B=1, H=2, L=2, d=2 from random values: o = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1
+    q, k, v = _rand(1, 2, 2, 2), _rand(1, 2, 2, 2), _rand(1, 2, 2, 2)
+    out = oracle.attention(q, k, v, 0.7)
+    for i in range(2):
+        for h in range(2):
+            s0 = 0.7 * (q[0, i, h, 0] * k[0, 0, h, 0] + q[0, i, h, 1] * k[0, 0, h, 1])
+            s1 = 0.7 * (q[0, i, h, 0] * k[0, 1, h, 0] + q[0, i, h, 1] * k[0, 1, h, 1])
+            w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+            w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+            np.testing.assert_allclose(out[0, i, h], w0 * v[0, 0, h] + w1 * v[0, 1, h], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("shape", [(1, 7, 2, 13, 16), (2, 33, 3, 65, 64), (1, 64, 4, 64, 128)])
+def test_attention_matches_torch_sdpa_float64(shape):
+    B, Lq, H, Lk, d = shape
+    q, k, v = _rand(B, Lq, H, d), _rand(B, Lk, H, d), _rand(B, Lk, H, d)
+    out = oracle.attention(q, k, v, d ** -0.5)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, d ** -0.5), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_causal_bottom_right_matches_masked_sdpa():
+    B, Lq, Lk, H, d = 1, 5, 12, 2, 8
+    q, k, v = _rand(B, Lq, H, d), _rand(B, Lk, H, d), _rand(B, Lk, H, d)
+    out = oracle.attention(q, k, v, 0.35, causal=True)
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lk)[None, :]
+    mask = torch.from_numpy(j <= i + (Lk - Lq))
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.35, mask=mask), rtol=1e-12, atol=1e-13)
+    # square causal equals torch's is_causal
+    q2, k2, v2 = _rand(2, 17, 2, 8), _rand(2, 17, 2, 8), _rand(2, 17, 2, 8)
+    np.testing.assert_allclose(oracle.attention(q2, k2, v2, 0.35, causal=True),
+                               _sdpa64(q2, k2, v2, 0.35, causal=True), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_key_permutation_invariance():
+    q, k, v = _rand(1, 6, 2, 16), _rand(1, 40, 2, 16), _rand(1, 40, 2, 16)
+    perm = RNG.permutation(40)
+    a = oracle.attention(q, k, v, 0.25)
+    b = oracle.attention(q, k[:, perm], v[:, perm], 0.25)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_score_shift_invariance_large_offset():
+    # k_j + u with q.u = const per query: every score of a row moves by the same amount (~ +1000)
+    d = 16
+    q, k, v = _rand(1, 3, 1, d), _rand(1, 25, 1, d), _rand(1, 25, 1, d)
+    u = q[0, 0, 0] / np.dot(q[0, 0, 0], q[0, 0, 0]) * 4000.0   # q0.u = 4000, scale 0.25 -> +1000
+    a = oracle.attention(q[:, :1], k, v, 0.25)
+    b = oracle.attention(q[:, :1], k + u, v, 0.25)
+    np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-10)
+    assert np.isfinite(b).all()
+
+
+def test_attention_constant_and_linear_in_v():
+    q, k = _rand(1, 5, 2, 8), _rand(1, 19, 2, 8)
+    c = _rand(8)
+    vc = np.broadcast_to(c, (1, 19, 2, 8)).copy()
+    np.testing.assert_allclose(oracle.attention(q, k, vc, 0.4), np.broadcast_to(c, (1, 5, 2, 8)),
+                               rtol=0, atol=1e-13)
+    v1, v2 = _rand(1, 19, 2, 8), _rand(1, 19, 2, 8)
+    lhs = oracle.attention(q, k, 2.0 * v1 - 3.0 * v2, 0.4)
+    rhs = 2.0 * oracle.attention(q, k, v1, 0.4) - 3.0 * oracle.attention(q, k, v2, 0.4)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_one_hot_limit():
+    q, k, v = _rand(1, 1, 1, 8), _rand(1, 30, 1, 8), _rand(1, 30, 1, 8)
+    k[0, 17, 0] = q[0, 0, 0] * 100.0   # score gap of hundreds: weight of every other key < e^-300
+    out = oracle.attention(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 17, 0], rtol=0, atol=1e-12)
+
+
+def test_attention_gqa_equals_repeated_kv_heads():
+    q, k, v = _rand(2, 9, 6, 16), _rand(2, 21, 2, 16), _rand(2, 21, 2, 16)
+    a = oracle.attention(q, k, v, 0.25)
+    b = oracle.attention(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), 0.25)
+    np.testing.assert_allclose(a, b, rtol=0, atol=0)
+
+
+def test_attention_scale_folds_into_query():
+    q, k, v = _rand(1, 6, 2, 32), _rand(1, 50, 2, 32), _rand(1, 50, 2, 32)
+    np.testing.assert_allclose(oracle.attention(q, k, v, 0.17), oracle.attention(0.17 * q, k, v, 1.0),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_attention_row_subset_equals_full():
+    q, k, v = _rand(2, 11, 3, 8), _rand(2, 13, 3, 8), _rand(2, 13, 3, 8)
+    full = oracle.attention(q, k, v, 0.3, causal=True)
+    rows = np.array([0, 5, 17, 65, 32, 2 * 11 * 3 - 1])
+    sub = oracle.attention(q, k, v, 0.3, causal=True, rows=rows)
+    np.testing.assert_array_equal(sub, full.reshape(-1, 8)[rows])
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+@pytest.mark.parametrize("case", _load("norm_rope_closed_form.json")["rmsnorm"], ids=lambda c: c["note"][:20])
+def test_rmsnorm_hand_worked(case):
+    out = oracle.rmsnorm(np.array([case["z"]]), np.array(case["gamma"]), case["eps"])
+    np.testing.assert_allclose(out[0], case["expected"], rtol=0, atol=1e-15)
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance_and_gamma_linearity():
+    z = _rand(50, 128)
+    one = oracle.rmsnorm(z, np.ones(128), 0.0)
+    np.testing.assert_allclose(np.sqrt((one ** 2).mean(axis=1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rmsnorm(7.5 * z, np.ones(128), 0.0), one, rtol=1e-14, atol=1e-15)
+    g1, g2 = _rand(128), _rand(128)
+    np.testing.assert_allclose(oracle.rmsnorm(z, 2 * g1 + g2, 1e-6),
+                               2 * oracle.rmsnorm(z, g1, 1e-6) + oracle.rmsnorm(z, g2, 1e-6),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_matches_torch_float64():
+    z, g = _rand(3, 7, 5, 64), _rand(64)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(z), (64,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rmsnorm(z, g, 1e-6), ref, rtol=1e-13, atol=1e-14)
+    # inner scope (m = H*d) is the same routine over a flattened token
+    zi = z.reshape(3, 7, 5 * 64)
+    gi = _rand(5 * 64)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(zi), (320,), torch.from_numpy(gi), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rmsnorm(zi, gi, 1e-6), ref, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------------------ RoPE
+
+@pytest.mark.parametrize("case", _load("norm_rope_closed_form.json")["rope"], ids=lambda c: c["note"][:20])
+def test_rope_hand_worked(case):
+    style = {"split": oracle.SPLIT, "interleaved": oracle.INTERLEAVED}[case["style"]]
+    z = np.array(case["z"]).reshape(1, 1, 1, 4)
+    out = oracle.rope(z, np.array([case["angles"]]), style)
+    np.testing.assert_allclose(out.reshape(-1), case["expected"], rtol=0, atol=1e-15)
+
+
+def _angles(positions, d):
+    return synthetic.rope_angles(positions, d).numpy().astype(np.float64)
+
+
+def test_rope_angle_table_values():
+    a = _angles([0, 1, 3000], 128)
+    assert np.all(a[0] == 0)
+    assert a[1, 0] == 1.0 and a[2, 0] == 3000.0
+    # omega_32 = 10000^(-64/128) = 1/100
+    np.testing.assert_allclose(a[1, 32], 0.01, rtol=1e-7)
+    np.testing.assert_allclose(a[2, 32], 30.0, rtol=1e-7)
+
+
+@pytest.mark.parametrize("style", [oracle.SPLIT, oracle.INTERLEAVED])
+def test_rope_preserves_pair_norms(style):
+    d = 64
+    z = _rand(2, 9, 3, d)
+    out = oracle.rope(z, _angles(np.arange(100, 109), d), style)
+    if style == oracle.SPLIT:
+        pa, pb = np.arange(d // 2), np.arange(d // 2) + d // 2
+    else:
+        pa, pb = np.arange(0, d, 2), np.arange(1, d, 2)
+    np.testing.assert_allclose(out[..., pa] ** 2 + out[..., pb] ** 2, z[..., pa] ** 2 + z[..., pb] ** 2,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_rope_relative_position_identity():
+    # <R_p q, R_p' k> = <R_(p-p') q, k> with angles p * omega_r (computed here in fp64)
+    d = 32
+    omega = 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+    q, k = _rand(1, 1, 1, d), _rand(1, 1, 1, d)
+    for p, pp in [(7, 3), (120, 119), (5, 40)]:
+        lhs = np.sum(oracle.rope(q, (p * omega)[None], oracle.SPLIT) * oracle.rope(k, (pp * omega)[None], oracle.SPLIT))
+        rhs = np.sum(oracle.rope(q, ((p - pp) * omega)[None], oracle.SPLIT) * k)
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_split_equals_interleaved_under_feature_permutation():
+    d = 16
+    z = _rand(1, 4, 2, d)
+    ang = _angles(np.arange(4), d)
+    perm = np.empty(d, dtype=int)          # interleaved position 2r <- split r, 2r+1 <- split r+d/2
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    split = oracle.rope(z, ang, oracle.SPLIT)
+    inter = oracle.rope(z[..., perm], ang, oracle.INTERLEAVED)
+    np.testing.assert_allclose(inter, split[..., perm], rtol=0, atol=1e-15)
+
+
+def test_rope_complex_multiplication_form():
+    d = 8
+    z = _rand(1, 3, 1, d)
+    ang = _angles([2, 50, 999], d)
+    out = oracle.rope(z, ang, oracle.INTERLEAVED)
+    zc = z[..., 0::2] + 1j * z[..., 1::2]
+    rc = zc * np.exp(1j * ang)[None, :, None, :]
+    np.testing.assert_allclose(out[..., 0::2], rc.real, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out[..., 1::2], rc.imag, rtol=1e-13, atol=1e-13)
+
+
+def test_qk_norm_rope_order_is_norm_then_rope():
+    d = 16
+    z, g = _rand(1, 3, 2, d), _rand(d)
+    ang = _angles([5, 6, 7], d)
+    out = oracle.qk_norm_rope(z, g, 1e-6, ang, oracle.SPLIT)
+    np.testing.assert_allclose(out, oracle.rope(oracle.rmsnorm(z, g, 1e-6), ang, oracle.SPLIT), rtol=0, atol=0)
+    # with gamma = 1 the rotation preserves the unit RMS of each head
+    out1 = oracle.qk_norm_rope(z, np.ones(d), 0.0, ang, oracle.SPLIT)
+    np.testing.assert_allclose(np.sqrt((out1 ** 2).mean(axis=-1)), 1.0, rtol=1e-13)
