@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the streaming-attention hot path on one MI355X.
+
+Default workload: long non-causal MHA forward [1, 20480, 56, 128] bf16 (scale 1/sqrt(128)), one
+attn_forward call per step. Other workloads (``--workload``) time the other configurations,
+including a full streaming self-attention step (prologue + cache append + attention).
+
+Prints ONE JSON line: metric/value (attention TFLOP/s = 4*B*H*Lq*Lk*d / step time), the
+dominant kernel's roofline (HIP-event timing of that kernel alone), and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·Lq·Lk·d) and % of bf16 MFMA peak, 1×MI355X"
+PEAK_MFMA_16BIT = 2516.6   # TFLOP/s, dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM = 8000.0          # GB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mha_20480_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "head_attention_streaming_amd", "csrc", "attn_fwd.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch measured with rocprofv3 PMC counters (committed summary), or None
+    when no summary exists or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"attn_fwd_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_workload(name: str, dev: str):
+    """Build device buffers and return (step_fn, kernel_fn, info)."""
+    import numpy as np
+    import torch
+
+    from head_attention_streaming_amd import binding, synthetic
+
+    if name == "copy_calibration":
+        # plain 16-byte vector copy of a known size (the cache-append kernel): 512 MiB read and
+        # 512 MiB written per launch; used to calibrate the HBM byte counters
+        n_tok, H, d = 16384, 128, 128   # 16384 * 128 * 128 * 2 B = 512 MiB
+        src = torch.empty((1, n_tok, H, d), dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+
+        def copy():
+            binding.kv_cache_append(None, src, None, dst, 0, 0, n_tok)
+        info = {"workload": name, "bytes_read": src.numel() * 2, "bytes_written": src.numel() * 2}
+        return None, copy, copy, info, None
+
+    w = synthetic.WORKLOADS[name]
+    info = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
+            "causal": w.causal, "scale": w.scale, "io_dtype": w.dtype, "prologue": w.prologue}
+    if w.prologue == "none":
+        q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        out = torch.empty_like(q)
+        fwd = binding.attn_forward if w.dtype == "bf16" else binding.attn_forward_f16
+
+        def step():
+            fwd(q, k, v, out, w.scale, w.causal)
+        return w, step, step, info, (q, k, v)
+
+    if w.prologue == "q_norm":
+        g = torch.Generator().manual_seed(w.seed)
+        q = synthetic.normal((w.B, w.Lq, w.Hq, w.d), "bf16", g).to(dev)
+        k = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g).to(dev)
+        v = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g).to(dev)
+        gq = synthetic.norm_weight(w.d, g).to(dev)
+        qs = torch.empty_like(q)
+        out = torch.empty_like(q)
+
+        def step():
+            binding.qk_norm_rope(q, qs, None, None, gq, None, None, 1e-6, binding.SA_NORM_HEAD, binding.SA_ROPE_NONE)
+            binding.attn_forward(qs, k, v, out, w.scale, False)
+
+        def kern():
+            binding.attn_forward(qs, k, v, out, w.scale, False)
+        info["step"] = "qk_norm_rope(Q only) + attn_forward"
+        return w, step, kern, info, (q, k, v)
+
+    # streaming self-attention: steady state (cache full, every step evicts the oldest chunk)
+    Lc, S = w.chunk, w.window
+    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, device=dev)
+    g = torch.Generator().manual_seed(w.seed)
+    gq, gk = synthetic.norm_weight(w.d, g).to(dev), synthetic.norm_weight(w.d, g).to(dev)
+    nsets = 6  # rotate input sets (6 x 55 MB) so the prologue and append are not served from cache
+    sets = []
+    for i in range(nsets):
+        gi = torch.Generator().manual_seed(w.seed + i)
+        sets.append([synthetic.normal((w.B, Lc, w.Hq, w.d), "bf16", gi).to(dev) for _ in range(3)])
+    q_buf = torch.empty((w.B, Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q_buf)
+    state = {"c": 0}
+    angles = [synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), w.d).to(dev) for c in range(8)]
+
+    def step():
+        c = state["c"]
+        q, k, v = sets[c % nsets]
+        binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[c % 8], 1e-6, w.scale)
+        state["c"] = c + 1
+
+    for _ in range(S // Lc):  # fill the cache before timing
+        step()
+
+    def kern():
+        binding.attn_forward_kvstride(q_buf, cache.k, cache.v, out, S, w.scale, False)
+    info["step"] = "qk_norm_rope(Q,K->cache) + kv_cache_append(V) + attn_forward_kvstride, cache full"
+    info["cache_tokens"] = S
+    return w, step, kern, info, None
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def cpu_baseline(w, tensors, target_s: float):
+    """The fp64 oracle on a bounded row sample of the same inputs; returns a dict."""
+    import numpy as np
+    import oracle
+    from head_attention_streaming_amd import synthetic
+
+    if tensors is None:  # streaming: time the attention rows of one full-cache step
+        import torch
+        g = torch.Generator().manual_seed(w.seed)
+        q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
+    else:
+        q, k, v = (t.cpu() for t in tensors)
+    dt = w.dtype
+    qn = oracle.decode(synthetic.bits(q), dt).reshape(q.shape)
+    kn = oracle.decode(synthetic.bits(k), dt).reshape(k.shape)
+    vn = oracle.decode(synthetic.bits(v), dt).reshape(v.shape)
+    total = w.B * w.Lq * w.Hq
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.sort(rng.choice(total, size=min(n, total), replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(qn, kn, vn, w.scale, w.causal, rows=rows, nthreads=threads)
+        return rows, time.perf_counter() - t0
+
+    n = max(threads * 4, 64)
+    rows, t = run(n)
+    while t < 0.5 and len(rows) < total:
+        n *= 4
+        rows, t = run(n)
+    n_full = min(total, int(len(rows) * target_s / max(t, 1e-6)))
+    if n_full > len(rows):
+        rows, t = run(n_full)
+    # flops of the sampled rows by the metric's formula (causal rows: their visible keys)
+    if w.causal:
+        i = (rows // w.Hq) % w.Lq
+        keys = np.minimum(w.Lk, i + (w.Lk - w.Lq) + 1).sum()
+        fl = 4.0 * w.d * float(keys)
+    else:
+        fl = 4.0 * w.d * w.Lk * len(rows)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {total} query rows (random, seed 0), each over all its keys; "
+                      f"{t:.1f} s wall, fp64, {threads} threads",
+            "seconds": round(t, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w, step, kern, info, tensors = make_workload(args.workload, dev)
+
+    torch.cuda.synchronize()
+    if w is None:  # calibration copy: report GB/s only
+        ms, _ = time_loop(step, args.steps, args.warmup)
+        gbs = (info["bytes_read"] + info["bytes_written"]) / (ms * 1e-3) / 1e9
+        print(json.dumps({"workload": info["workload"], "ms": round(ms, 4), "GB/s": round(gbs, 1), **info}))
+        return
+    ms_step, wall_ms = time_loop(step, args.steps, args.warmup)
+    ms_kern, _ = time_loop(kern, args.steps, 2) if kern is not step else (ms_step, wall_ms)
+
+    flops = w.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_kern * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": dict(info, flops_per_step=flops, pct_of_bf16_peak=round(100 * value / PEAK_MFMA_16BIT, 2),
+                       wall_ms_per_step=round(wall_ms, 4)),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_16BIT, 4), "traffic": traffic,
+                     "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'}>",
+                     "kernel_ms": round(ms_kern, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""Python binding of libstreamattn.so: the C entry points under the same names.
+
+Argument marshalling only -- tensors supply device pointers and shapes, the current PyTorch
+HIP stream supplies the stream, and a non-zero status raises ``StreamAttnError`` with the
+library's message. Every computation runs in the library's HIP kernels; there is no
+fallback path, and a missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+SA_DTYPE_BF16, SA_DTYPE_F16 = 0, 1
+SA_NORM_NONE, SA_NORM_HEAD = 0, 1
+SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED = 0, 1, 2
+
+EXPORTS = ("qk_norm_rope", "kv_cache_slot", "kv_cache_append", "attn_forward", "attn_forward_f16",
+           "attn_forward_kvstride", "sa_last_error")
+
+_lib = None
+
+
+class StreamAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} returned {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """Load libstreamattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m head_attention_streaming_amd.build`")
+        L = ctypes.CDLL(path)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.qk_norm_rope.argtypes = [P, P, I64, P, P, I64, P, P, P, I, I, I, I, I, F, I, I, P]
+        L.kv_cache_slot.argtypes = [I64, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I)]
+        L.kv_cache_append.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, P]
+        L.attn_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
+        L.attn_forward_f16.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
+        L.attn_forward_kvstride.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I64, I, P]
+        L.sa_last_error.restype = ctypes.c_char_p
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise StreamAttnError(fn, status, lib().sa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t=None):
+    dev = t.device if t is not None and t.is_cuda else None
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return SA_DTYPE_F16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def attn_forward(q, k, v, out, scale: float, causal: bool = False):
+    """out[B, Lq, Hq, d] = softmax(q k^T * scale) v for bf16 q/k/v/out (contiguous)."""
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    _check("attn_forward", lib().attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lk, d,
+                                              float(scale), int(bool(causal)), _stream(q)))
+    return out
+
+
+def attn_forward_f16(q, k, v, out, scale: float, causal: bool = False):
+    """The fp16 variant of attn_forward."""
+    B, Lq, Hq, d = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    _check("attn_forward_f16", lib().attn_forward_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, Lk,
+                                                      d, float(scale), int(bool(causal)), _stream(q)))
+    return out
+
+
+def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = False):
+    """Attention over the first Lk tokens of k, v [B, S, Hkv, d] (S >= Lk), e.g. a rolling cache."""
+    B, Lq, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    kv_bstride = S * Hkv * d
+    _check("attn_forward_kvstride",
+           lib().attn_forward_kvstride(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, int(Lk), d,
+                                       float(scale), int(bool(causal)), kv_bstride, _dtype_code(q), _stream(q)))
+    return out
+
+
+def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None, angles=None, eps: float = 1e-6,
+                 norm_scope: int = SA_NORM_HEAD, rope_style: int = SA_ROPE_SPLIT, q_out_bstride=None,
+                 k_out_bstride=None, Hkv: int | None = None):
+    """Per-head RMSNorm then RoPE of q_in (and k_in) into q_out (and k_out), bf16.
+
+    q_in [B, L, Hq, d]; k_out may be a view of a cache row range (pass k_out_bstride = S*Hkv*d).
+    """
+    B, L, Hq, d = q_in.shape
+    if Hkv is None:
+        Hkv = k_in.shape[2] if k_in is not None else 0
+    if q_out_bstride is None:
+        q_out_bstride = L * Hq * d
+    if k_out_bstride is None:
+        k_out_bstride = L * Hkv * d
+    _check("qk_norm_rope", lib().qk_norm_rope(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
+                                              k_out_bstride, _ptr(gamma_q), _ptr(gamma_k), _ptr(angles), B, L, Hq,
+                                              Hkv, d, float(eps), norm_scope, rope_style, _stream(q_in)))
+
+
+def kv_cache_slot(chunk_idx: int, chunk_len: int, sink_size: int, window_size: int):
+    """(slot_base, visible_len) of chunk ``chunk_idx`` in a rolling sink + window cache."""
+    slot = ctypes.c_int64()
+    vis = ctypes.c_int()
+    _check("kv_cache_slot", lib().kv_cache_slot(int(chunk_idx), int(chunk_len), int(sink_size), int(window_size),
+                                                ctypes.byref(slot), ctypes.byref(vis)))
+    return slot.value, vis.value
+
+
+def kv_cache_append(k_new, v_new, cache_k, cache_v, chunk_idx: int, sink_size: int, window_size: int):
+    """Copy k_new / v_new [B, Lc, Hkv, d] (either may be None) into their cache slot range."""
+    ref = v_new if v_new is not None else k_new
+    B, Lc, Hkv, d = ref.shape
+    _check("kv_cache_append", lib().kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B, Lc,
+                                                    Hkv, d, sink_size, window_size, int(chunk_idx), _stream(ref)))
+
+
+class BlockKVCache:
+    """Caller-side rolling cache: storage [B, sink + window, Hkv, d] plus the chunk bookkeeping.
+
+    Lifecycle per chunk (page "Accelerated building blocks", section "Cache lifecycle"):
+    before_update(c) -> write this chunk's keys/values -> attend -> after_update(c).
+    """
+
+    def __init__(self, B: int, Hkv: int, d: int, chunk_len: int, sink_size: int, window_size: int,
+                 dtype=torch.bfloat16, device="cuda"):
+        self.B, self.Hkv, self.d = B, Hkv, d
+        self.chunk_len, self.sink_size, self.window_size = chunk_len, sink_size, window_size
+        S = sink_size + window_size
+        self.k = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
+        self.v = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
+        self.slot_base = 0
+        self.visible_len = 0
+        self._current = None
+
+    @property
+    def capacity(self) -> int:
+        return self.sink_size + self.window_size
+
+    def before_update(self, chunk_idx: int):
+        if self._current is not None:
+            raise RuntimeError("before_update called twice without after_update")
+        self.slot_base, self.visible_len = kv_cache_slot(chunk_idx, self.chunk_len, self.sink_size,
+                                                         self.window_size)
+        self._current = chunk_idx
+        return self.slot_base, self.visible_len
+
+    def k_slot_view(self):
+        """Keys of the current chunk's slot range (a strided view into the cache)."""
+        return self.k[:, self.slot_base:self.slot_base + self.chunk_len]
+
+    def after_update(self, chunk_idx: int):
+        if self._current != chunk_idx:
+            raise RuntimeError("after_update does not match before_update")
+        self._current = None
+
+
+def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
+                               gamma_k, angles, eps: float, scale: float,
+                               rope_style: int = SA_ROPE_SPLIT):
+    """One streaming self-attention chunk with before-cache RoPE, as four library calls:
+
+    before_update -> qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot) ->
+    kv_cache_append (v_in -> cache values) -> attn_forward_kvstride over the visible cache ->
+    after_update. Returns the visible length used.
+    """
+    slot, visible = cache.before_update(chunk_idx)
+    S = cache.capacity
+    qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, angles, eps,
+                 SA_NORM_HEAD, rope_style, k_out_bstride=S * cache.Hkv * cache.d)
+    kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
+    attn_forward_kvstride(q_buf, cache.k, cache.v, out, visible, scale, False)
+    cache.after_update(chunk_idx)
+    return visible

@@ -1,0 +1,343 @@
+// Attention forward kernel for gfx950 (MI355X): out = softmax(Q K^T * scale) V per head.
+//
+// The operation is the scaled dot-product attention equation of the page
+// "flashdreams.accelerated", section "Multi Head Attention Definition". It is evaluated as an
+// exact tiled attention with an online softmax (the IO-aware tiling the FlashAttention papers
+// describe, which the "optimizing-attention-flash" page cites): keys are streamed in tiles, a
+// running row maximum m and row sum l are kept in registers, and the partial output is
+// rescaled by exp2(m_old - m_new) whenever the maximum grows. No score matrix is stored.
+//
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one (batch, head)):
+//   * each wave owns 32 query rows; its Q^T slice stays in registers as the MFMA B operand;
+//   * K and V tiles of 64 keys are staged global -> registers -> LDS, double buffered, so the
+//     next tile's global loads are in flight while the current tile is computed;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16 (bf16 or f16): each lane then holds 16 scores of ONE
+//     query column, so row max/sum are in-lane reductions plus one v_permlane32_swap;
+//   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16: the score registers, converted to f16, are
+//     directly the B operand (no shuffle); V^T comes from LDS through ds_read_b64_tr_b16,
+//     which returns 4 consecutive keys of one feature column per lane;
+//   * exp2 with log2(e) folded into the scale; the output is divided by l once at the end.
+// Probabilities use f16 (11-bit significand) for the P*V product; bf16 V is converted to f16
+// when it is staged into LDS (exact for |v| in [2^-17, 65504]).
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBM = 128;      // query rows per workgroup
+constexpr int kBN = 64;       // keys per tile
+constexpr int kThreads = 256; // 4 waves
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct KParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    int Hq, Hkv, Lq, Lk, group, n_qblk, causal, nblocks;
+    int64_t q_bstride, kv_bstride;
+    int q_tstride, kv_tstride;
+    float c;  // scale * log2(e)
+};
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 8 bf16 -> 8 f16 (exact in f16's normal range).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
+    uint4 r;
+    r.x = pack_f16x2(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u));
+    r.y = pack_f16x2(__uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    r.z = pack_f16x2(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xffff0000u));
+    r.w = pack_f16x2(__uint_as_float(x.w << 16), __uint_as_float(x.w & 0xffff0000u));
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_qk(uint4 a, uint4 b, f32x16 c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// max / sum of a value with its copy in the other 32-lane half of the wave
+__device__ __forceinline__ float half_swap_max(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
+    constexpr int KST = D + 8;    // LDS row stride of a K tile (elements): conflict-free b128 reads
+    constexpr int VST = D + 32;   // LDS row stride of a V tile: conflict-free transposed reads
+    constexpr int DC = D / 16;    // QK MFMAs per 32-key block (16 features each)
+    constexpr int DB = D / 32;    // 32-feature blocks of the O^T accumulator
+    constexpr int CPR = D / 8;    // 16-byte chunks per key row
+    constexpr int NCH = kBN * CPR / kThreads;  // 16-byte chunks each thread stages per tile
+    static_assert(NCH * kThreads == kBN * CPR, "tile must split evenly over the workgroup");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KST];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VST];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;   // half of the wave
+    const int j = lane & 31;   // query column owned by this lane
+
+    // Workgroups are dealt round-robin to the 8 XCDs; regroup them so that each XCD works on a
+    // contiguous range of (batch, head, query block) and its L2 serves the same K/V head.
+    int bid = blockIdx.x;
+    {
+        const int nb = p.nblocks, base = nb >> 3, rem = nb & 7, x = bid & 7;
+        bid = x * base + (x < rem ? x : rem) + (bid >> 3);
+    }
+    int qblk = bid % p.n_qblk;
+    const int bh = bid / p.n_qblk;
+    const int h = bh % p.Hq;
+    const int b = bh / p.Hq;
+    if (p.causal) qblk = p.n_qblk - 1 - qblk;  // longest rows first
+    const int hk = h / p.group;
+
+    const int qb0 = qblk * kBM;
+    const int q0w = qb0 + wave * 32;
+    const int shift = p.Lk - p.Lq;  // causal: query i sees keys j <= i + shift
+
+    int kend = p.Lk;
+    if (p.causal) {
+        const int qlast = min(qb0 + kBM, p.Lq) - 1;
+        kend = min(p.Lk, qlast + shift + 1);
+    }
+    const int nkt = (kend + kBN - 1) / kBN;
+
+    // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of query row q0w + j.
+    uint4 qf[DC];
+    {
+        const int qrow = min(q0w + j, p.Lq - 1);
+        const uint16_t* qp = p.q + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D + 8 * g;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const uint4*>(qp + 16 * c);
+    }
+
+    const uint16_t* kbase = p.k + b * p.kv_bstride + hk * D;
+    const uint16_t* vbase = p.v + b * p.kv_bstride + hk * D;
+
+    uint4 kreg[NCH], vreg[NCH];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int id = tid + kThreads * u;
+            const int row = id / CPR, col = (id % CPR) * 8;
+            const int key = min(kt * kBN + row, p.Lk - 1);  // tail keys re-read a valid row; masked below
+            const int64_t off = (int64_t)key * p.kv_tstride + col;
+            kreg[u] = *reinterpret_cast<const uint4*>(kbase + off);
+            vreg[u] = *reinterpret_cast<const uint4*>(vbase + off);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int id = tid + kThreads * u;
+            const int row = id / CPR, col = (id % CPR) * 8;
+            *reinterpret_cast<uint4*>(&Ks[buf][row * KST + col]) = kreg[u];
+            *reinterpret_cast<uint4*>(&Vs[buf][row * VST + col]) = BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+        }
+    };
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_run = -1e30f;  // running max of scaled scores (log2 domain); finite so exp2 never sees inf-inf
+    float l_run = 0.f;     // this lane's share of the running row sum
+
+    const float c = p.c;
+    const int qabs = q0w + j;
+    // last key any row of this wave may see; tiles past it hold no visible key for this wave
+    const int wave_klast = p.causal ? min(q0w + 31, p.Lq - 1) + shift : p.Lk - 1;
+    const int wave_kfirst_masked = p.causal ? q0w + shift + 1 : p.Lk;  // first key masked for some row
+
+    // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
+    // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
+    const int G = lane >> 4, L16 = lane & 15;
+    const int vrow_lane = 4 * (G >> 1) + (L16 >> 2);
+    const int vcol_lane = 16 * (G & 1) + 4 * (L16 & 3);
+
+    if (nkt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nkt) load_tile(kt + 1);
+
+        const int k0 = kt * kBN;
+        if (k0 <= wave_klast) {
+            // ---- S^T = K Q^T : two 32-key blocks
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                const uint16_t* kp = &Ks[buf][(kb * 32 + j) * KST + 8 * g];
+#pragma unroll
+                for (int cc = 0; cc < DC; ++cc)
+                    s[kb] = mfma_qk<BF16>(*reinterpret_cast<const uint4*>(kp + 16 * cc), qf[cc], s[kb]);
+            }
+            // ---- mask tail keys and keys beyond the causal diagonal
+            if (k0 + kBN > p.Lk || k0 + kBN - 1 >= wave_kfirst_masked) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const bool ok = key < p.Lk && (!p.causal || key <= qabs + shift);
+                        if (!ok) s[kb][r] = -INFINITY;
+                    }
+            }
+            // ---- online softmax (log2 domain)
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = half_swap_max(mx);
+            const float m_new = fmaxf(m_run, mx * c);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            float lsum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_new));
+                    s[kb][r] = e;
+                    lsum += e;
+                }
+            l_run = l_run * alpha + lsum;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+            // ---- P^T operands (f16): registers 8hh..8hh+7 of block kb cover 16 keys
+            uint4 pf[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    pf[kb][hh].x = pack_f16x2(s[kb][8 * hh + 0], s[kb][8 * hh + 1]);
+                    pf[kb][hh].y = pack_f16x2(s[kb][8 * hh + 2], s[kb][8 * hh + 3]);
+                    pf[kb][hh].z = pack_f16x2(s[kb][8 * hh + 4], s[kb][8 * hh + 5]);
+                    pf[kb][hh].w = pack_f16x2(s[kb][8 * hh + 6], s[kb][8 * hh + 7]);
+                }
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int row0 = kb * 32 + 16 * hh + vrow_lane;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const uint16_t* vp = &Vs[buf][row0 * VST + 32 * db + vcol_lane];
+                        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+                        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * VST));
+                        const i16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                        const f16x8 a = __builtin_bit_cast(f16x8, a8);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pf[kb][hh]),
+                                                                        o[db], 0, 0, 0);
+                    }
+                }
+        }
+
+        if (kt + 1 < nkt) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
+    const float l = half_swap_sum(l_run);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qabs < p.Lq) {
+        uint16_t* op = p.out + b * p.q_bstride + (int64_t)qabs * p.q_tstride + h * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int dcol = 32 * db + 8 * rg + 4 * g;
+                const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
+                const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
+                uint2 w;
+                if constexpr (BF16) {
+                    w.x = pack_bf16x2(x0, x1);
+                    w.y = pack_bf16x2(x2, x3);
+                } else {
+                    w.x = pack_f16x2(x0, x1);
+                    w.y = pack_f16x2(x2, x3);
+                }
+                *reinterpret_cast<uint2*>(op + dcol) = w;
+            }
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+    KParams p;
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.out = static_cast<uint16_t*>(a.out);
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.Lq = a.Lq;
+    p.Lk = a.Lk;
+    p.group = a.Hq / a.Hkv;
+    p.n_qblk = (a.Lq + kBM - 1) / kBM;
+    p.causal = a.causal;
+    p.q_bstride = a.q_bstride;
+    p.kv_bstride = a.kv_bstride;
+    p.q_tstride = a.Hq * D;
+    p.kv_tstride = a.Hkv * D;
+    p.c = a.scale * kLog2e;
+    const int64_t nblocks = (int64_t)p.n_qblk * a.Hq * a.B;
+    p.nblocks = (int)nblocks;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+    const bool bf16 = a.dtype == 0;
+    if (a.d == 128) return bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+    return bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+}  // namespace sa

@@ -1,0 +1,229 @@
+// C entry points of libstreamattn.so (declared in include/streamattn.h): host-side argument
+// validation, the rolling-cache slot rule, and dispatch to the gfx950 kernels. Nothing here
+// allocates device memory or synchronises; every failure is reported before any launch.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_internal.h"
+#include "streamattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+// element count a*b*c*d without overflow (int64), -1 if it would overflow
+int64_t mul4(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const int64_t lim = INT64_C(1) << 62;
+    int64_t r = 1;
+    for (int64_t x : {a, b, c, d}) {
+        if (x != 0 && r > lim / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+int check_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
+               int Lk, int d, float scale, int causal, int64_t kv_bstride, int dtype) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Lq < 0 || Lk < 0)
+        return fail(SA_ERR_RANGE, "attn_forward: negative or zero size (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d)", B, Hq,
+                    Hkv, Lq, Lk);
+    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16)
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0) or f16 (1)", dtype);
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward: head dim %d not built (64, 128)", d);
+    if (Hq % Hkv != 0) return fail(SA_ERR_SHAPE, "attn_forward: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (causal != 0 && causal != 1) return fail(SA_ERR_RANGE, "attn_forward: causal must be 0 or 1");
+    if (causal && Lq > Lk) return fail(SA_ERR_SHAPE, "attn_forward: causal needs Lq <= Lk (Lq=%d Lk=%d)", Lq, Lk);
+    if (!(scale > 0.f) || scale > 1e30f) return fail(SA_ERR_RANGE, "attn_forward: scale must be positive and finite");
+    if (B == 0 || Lq == 0) return SA_OK + 1;  // nothing to do
+    if (Lk == 0) return fail(SA_ERR_SHAPE, "attn_forward: Lk must be >= 1 when Lq > 0");
+    if (!q || !k || !v || !out) return fail(SA_ERR_NULL, "attn_forward: null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SA_ERR_ALIGN, "attn_forward: tensor pointers must be 16-byte aligned");
+    const int64_t nq = mul4(B, Lq, Hq, d);
+    const int64_t nkv = mul4(1, Lk, Hkv, d);
+    if (nq < 0 || nkv < 0 || (int64_t)Lq * Hq * d > INT32_MAX || (int64_t)Lk * Hkv * d > INT64_C(1) << 40)
+        return fail(SA_ERR_RANGE, "attn_forward: tensor too large");
+    if (kv_bstride < nkv) return fail(SA_ERR_SHAPE, "attn_forward: kv_bstride %lld < Lk*Hkv*d %lld",
+                                      (long long)kv_bstride, (long long)nkv);
+    if (kv_bstride % 8) return fail(SA_ERR_ALIGN, "attn_forward: kv_bstride must be a multiple of 8 elements");
+    if (mul4(B, kv_bstride, 1, 1) < 0) return fail(SA_ERR_RANGE, "attn_forward: K/V extent overflows");
+    const int64_t nblocks = (int64_t)((Lq + 127) / 128) * Hq * B;
+    if (nblocks > INT32_MAX) return fail(SA_ERR_RANGE, "attn_forward: grid too large");
+    return SA_OK;
+}
+
+int run_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+             float scale, int causal, int64_t kv_bstride, int dtype, void* stream) {
+    const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, kv_bstride, dtype);
+    if (st < 0) return st;
+    if (st > 0) return ok();
+    sa::AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.d = d;
+    a.q_bstride = (int64_t)Lq * Hq * d;
+    a.kv_bstride = kv_bstride;
+    a.scale = scale;
+    a.causal = causal;
+    a.dtype = dtype;
+    return hip_status(sa::launch_attn_fwd(a, static_cast<hipStream_t>(stream)), "attn_forward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_last_error(void) { return g_err; }
+
+int attn_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk,
+                 int d, float scale, int causal, void* stream) {
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, (int64_t)Lk * Hkv * d, SA_DTYPE_BF16,
+                    stream);
+}
+
+int attn_forward_f16(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
+                     int Lk, int d, float scale, int causal, void* stream) {
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, (int64_t)Lk * Hkv * d, SA_DTYPE_F16,
+                    stream);
+}
+
+int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
+                          int Lk, int d, float scale, int causal, int64_t kv_bstride, int dtype, void* stream) {
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, kv_bstride, dtype, stream);
+}
+
+int kv_cache_slot(int64_t chunk_idx, int chunk_len, int sink_size, int window_size, int64_t* slot_base_out,
+                  int* visible_len_out) {
+    if (!slot_base_out || !visible_len_out) return fail(SA_ERR_NULL, "kv_cache_slot: null output pointer");
+    if (chunk_idx < 0 || chunk_len <= 0 || sink_size < 0 || window_size < chunk_len)
+        return fail(SA_ERR_RANGE, "kv_cache_slot: need chunk_idx >= 0, chunk_len > 0, sink >= 0, window >= chunk");
+    if (sink_size % chunk_len || window_size % chunk_len)
+        return fail(SA_ERR_RANGE, "kv_cache_slot: sink (%d) and window (%d) must be multiples of chunk_len (%d)",
+                    sink_size, window_size, chunk_len);
+    if ((int64_t)sink_size + window_size > INT32_MAX) return fail(SA_ERR_RANGE, "kv_cache_slot: cache too large");
+    const int64_t n_sink = sink_size / chunk_len;
+    const int64_t n_win = window_size / chunk_len;
+    const int64_t cap = (int64_t)sink_size + window_size;
+    if (chunk_idx < n_sink)
+        *slot_base_out = chunk_idx * chunk_len;
+    else
+        *slot_base_out = sink_size + ((chunk_idx - n_sink) % n_win) * chunk_len;
+    const int64_t seen = chunk_idx >= cap / chunk_len ? cap : (chunk_idx + 1) * chunk_len;
+    *visible_len_out = (int)(seen < cap ? seen : cap);
+    return ok();
+}
+
+int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* cache_v, int B, int Lc, int Hkv,
+                    int d, int sink_size, int window_size, int64_t chunk_idx, void* stream) {
+    int64_t slot = 0;
+    int vis = 0;
+    const int st = kv_cache_slot(chunk_idx, Lc, sink_size, window_size, &slot, &vis);
+    if (st != SA_OK) return st;
+    if (B < 0 || Hkv <= 0) return fail(SA_ERR_RANGE, "kv_cache_append: B >= 0 and Hkv > 0 required");
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "kv_cache_append: head dim %d not built (64, 128)", d);
+    if (!k_new && !v_new) return fail(SA_ERR_NULL, "kv_cache_append: both k_new and v_new are NULL");
+    if ((k_new && !cache_k) || (v_new && !cache_v)) return fail(SA_ERR_NULL, "kv_cache_append: null cache pointer");
+    for (const void* p : {k_new, v_new, (const void*)cache_k, (const void*)cache_v})
+        if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "kv_cache_append: pointers must be 16-byte aligned");
+    const int64_t row = (int64_t)Hkv * d;
+    const int64_t chunk_elems = mul4(Lc, row, 1, 1);
+    const int64_t cap = (int64_t)sink_size + window_size;
+    if (chunk_elems < 0 || mul4(B, cap, row, 1) < 0) return fail(SA_ERR_RANGE, "kv_cache_append: tensor too large");
+    if (B == 0) return ok();
+    const int64_t nvec = chunk_elems / 8;
+    if ((nvec + 1023) / 1024 > INT32_MAX || B > 65535) return fail(SA_ERR_RANGE, "kv_cache_append: grid too large");
+    for (int which = 0; which < 2; ++which) {
+        const void* src = which ? v_new : k_new;
+        void* dst = which ? cache_v : cache_k;
+        if (!src) continue;
+        sa::CopyArgs c;
+        c.src = src;
+        c.dst = dst;
+        c.B = B;
+        c.row_elems = chunk_elems;
+        c.dst_bstride = cap * row;
+        c.dst_offset = slot * row;
+        const int s = hip_status(sa::launch_copy_rows(c, static_cast<hipStream_t>(stream)), "kv_cache_append launch");
+        if (s != SA_OK) return s;
+    }
+    return ok();
+}
+
+int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
+                 int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
+                 int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, void* stream) {
+    if (B < 0 || L < 0 || Hq <= 0 || (k_in && Hkv <= 0))
+        return fail(SA_ERR_RANGE, "qk_norm_rope: negative or zero size");
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: head dim %d not built (64, 128)", d);
+    if (norm_scope != SA_NORM_NONE && norm_scope != SA_NORM_HEAD)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: norm scope %d not built (none, head)", norm_scope);
+    if (rope_style < SA_ROPE_NONE || rope_style > SA_ROPE_INTERLEAVED)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: unknown RoPE style %d", rope_style);
+    if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "qk_norm_rope: eps must be >= 0 and finite");
+    if (B == 0 || L == 0) return ok();
+    if (!q_in || !q_out) return fail(SA_ERR_NULL, "qk_norm_rope: null q pointer");
+    if ((k_in == nullptr) != (k_out == nullptr)) return fail(SA_ERR_NULL, "qk_norm_rope: k_in and k_out must both be set or both NULL");
+    if (norm_scope == SA_NORM_HEAD && (!gamma_q || (k_in && !gamma_k)))
+        return fail(SA_ERR_NULL, "qk_norm_rope: RMSNorm weights required for head scope");
+    if (norm_scope == SA_NORM_NONE && (gamma_q || gamma_k))
+        return fail(SA_ERR_SHAPE, "qk_norm_rope: weights given with norm scope none");
+    if ((rope_style != SA_ROPE_NONE) != (rope_angles != nullptr))
+        return fail(SA_ERR_NULL, "qk_norm_rope: angles must be given iff RoPE is enabled");
+    for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out})
+        if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "qk_norm_rope: pointers must be 16-byte aligned");
+    const int64_t nq = mul4(1, L, Hq, d);
+    if (nq < 0 || mul4(B, L, k_in ? Hkv : 1, d) < 0) return fail(SA_ERR_RANGE, "qk_norm_rope: tensor too large");
+    if (q_out_bstride < nq || q_out_bstride % 8) return fail(SA_ERR_SHAPE, "qk_norm_rope: bad q_out_bstride");
+    if (k_in && (k_out_bstride < (int64_t)L * Hkv * d || k_out_bstride % 8))
+        return fail(SA_ERR_SHAPE, "qk_norm_rope: bad k_out_bstride");
+    if ((int64_t)B * L > INT32_MAX) return fail(SA_ERR_RANGE, "qk_norm_rope: grid too large");
+    sa::NormRopeArgs a;
+    a.q_in = q_in;
+    a.q_out = q_out;
+    a.q_out_bstride = q_out_bstride;
+    a.k_in = k_in;
+    a.k_out = k_out;
+    a.k_out_bstride = k_out_bstride;
+    a.gamma_q = gamma_q;
+    a.gamma_k = gamma_k;
+    a.angles = rope_angles;
+    a.B = B;
+    a.L = L;
+    a.Hq = Hq;
+    a.Hkv = k_in ? Hkv : 0;
+    a.d = d;
+    a.eps = eps;
+    a.norm_scope = norm_scope;
+    a.rope_style = rope_style;
+    return hip_status(sa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "qk_norm_rope launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// Q/K prologue for gfx950: per-head RMSNorm, then RoPE, one rounding to bf16.
+//
+// Page "flashdreams.accelerated", section "Multi Head Attention Definition": RMSNorm with head
+// scope maps each head's feature vector z (m = d) to gamma * z / sqrt(mean(z^2) + eps); RoPE then
+// rotates feature pair r of position p by theta_{p,r} (split-half pairs (r, r + d/2) or
+// interleaved pairs (2r, 2r + 1)); normalisation comes before RoPE, and V is untouched.
+//
+// Memory-bound: each element is read once and written once. One workgroup handles one token
+// (all query heads, then all key heads), so the token's d/2 angles are turned into cos/sin once
+// (in LDS) and reused by every head. A head row of d features is spread over d/8 lanes holding 8
+// features (one 16-byte load/store) each; the RMS reduction and the split-half partner exchange
+// are lane shuffles inside that group.
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(a[i] << 16);
+        f[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+    uint32_t a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 v = {f[2 * i], f[2 * i + 1]};
+        a[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+    return make_uint4(a[0], a[1], a[2], a[3]);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) qk_norm_rope_kernel(NormRopeArgs a) {
+    constexpr int LPR = D / 8;            // lanes per head row
+    constexpr int RPP = kThreads / LPR;   // head rows per pass
+    constexpr int HALF = D / 2;
+    __shared__ float cs[HALF], sn[HALF];
+
+    const int tok = blockIdx.x;           // b * L + p
+    const int b = tok / a.L, p = tok % a.L;
+    const int tid = threadIdx.x;
+    const int li = tid % LPR;             // which 8-feature slice of the row
+    const int rs = tid / LPR;             // row slot within a pass
+    const int f0 = 8 * li;
+
+    if (a.rope_style != 0) {
+        for (int r = tid; r < HALF; r += kThreads) {
+            float s, c;
+            sincosf(a.angles[(int64_t)p * HALF + r], &s, &c);
+            cs[r] = c;
+            sn[r] = s;
+        }
+    }
+    __syncthreads();
+
+    // cos/sin of the pairs this lane touches (identical for every head of the token)
+    float c8[8], s8[8];
+    if (a.rope_style == 1) {          // split: features f0..f0+7 belong to pairs (f0 % HALF) + e
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            c8[e] = cs[(f0 % HALF) + e];
+            s8[e] = sn[(f0 % HALF) + e];
+        }
+    } else if (a.rope_style == 2) {   // interleaved: pairs f0/2 + e for e < 4
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            c8[e] = cs[f0 / 2 + e];
+            s8[e] = sn[f0 / 2 + e];
+        }
+    }
+
+    float gq[8], gk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        gq[e] = a.norm_scope ? a.gamma_q[f0 + e] : 1.f;
+        gk[e] = (a.norm_scope && a.k_in) ? a.gamma_k[f0 + e] : 1.f;
+    }
+
+    const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
+    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + ((int64_t)b * a.L + p) * a.Hq * D;
+    const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
+    uint16_t* qout = static_cast<uint16_t*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
+    uint16_t* kout = a.k_out ? static_cast<uint16_t*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
+
+    // rows_padded keeps every lane of a row group inside the loop (shuffles need all of them)
+    const int rows_padded = (rows + RPP - 1) / RPP * RPP;
+    for (int row = rs; row < rows_padded; row += RPP) {
+        const bool valid = row < rows;
+        const bool is_q = row < a.Hq;
+        float z[8];
+        if (valid) {
+            const uint16_t* src = is_q ? qin + row * D : kin + (row - a.Hq) * D;
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(src + f0), z);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = 0.f;
+        }
+        if (a.norm_scope) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
+            ss = group_sum<LPR>(ss);
+            const float r = 1.f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
+        }
+        float o[8];
+        if (a.rope_style == 1) {
+            const bool first = li < LPR / 2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float other = __shfl_xor(z[e], LPR / 2);
+                o[e] = first ? c8[e] * z[e] - s8[e] * other : s8[e] * other + c8[e] * z[e];
+            }
+        } else if (a.rope_style == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = z[2 * e], x1 = z[2 * e + 1];
+                o[2 * e] = c8[e] * x0 - s8[e] * x1;
+                o[2 * e + 1] = s8[e] * x0 + c8[e] * x1;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = z[e];
+        }
+        if (valid) {
+            uint16_t* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
+            *reinterpret_cast<uint4*>(dst + f0) = pack_bf16x8(o);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.L));
+    if (a.d == 128)
+        hipLaunchKernelGGL(qk_norm_rope_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(qk_norm_rope_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace sa

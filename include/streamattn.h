@@ -1,0 +1,166 @@
+/*
+ * streamattn -- forward multi-head attention for streaming video models on MI355X (gfx950).
+ *
+ * C ABI of libstreamattn.so. Plain pointers and sizes only; no framework types.
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) unless stated otherwise.
+ *   - Layouts are token-major and contiguous in the last dimension:
+ *       queries / outputs  [B, Lq, Hq, d]
+ *       keys / values      [B, Lk, Hkv, d]
+ *     This is the [batch, length, heads, head_dim] layout of the page "flashdreams.accelerated",
+ *     section "Multi Head Attention Definition" (reshaped Q, K, V) and of its FlashAttention2
+ *     backend description (token-major queries, keys and values).
+ *   - 16-bit element types: bfloat16 (SA_DTYPE_BF16) or IEEE binary16 (SA_DTYPE_F16). The
+ *     accelerated-module guide restricts inputs to FP16/BF16 and head dims to powers of two in
+ *     [16, 256]; this library builds d = 64 and d = 128 and rejects the rest with
+ *     SA_ERR_UNSUPPORTED (no fallback kernel is ever substituted).
+ *   - Element strides and offsets are int64.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *     enqueues kernels on that stream and returns; none synchronises.
+ *   - Ownership: the caller allocates and frees every buffer, including the K/V cache. The
+ *     library allocates no device memory and keeps no pointer after a call returns.
+ *   - Errors: arguments are validated on the host before anything is launched. A negative
+ *     status means nothing was enqueued by that call (except SA_ERR_HIP, which reports a failed
+ *     launch). sa_last_error() returns a thread-local text for the last failing call.
+ *   - Base pointers must be 16-byte aligned (SA_ERR_ALIGN otherwise).
+ */
+#ifndef STREAMATTN_H
+#define STREAMATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_NULL = -1,        /* a required pointer is NULL */
+    SA_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. Hq % Hkv != 0, causal with Lq > Lk) */
+    SA_ERR_UNSUPPORTED = -3, /* valid request outside what is built (e.g. d not in {64, 128}) */
+    SA_ERR_ALIGN = -4,       /* a base pointer or stride is not 16-byte aligned */
+    SA_ERR_RANGE = -5,       /* a size is negative or an element count overflows */
+    SA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+} sa_status;
+
+enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1 };
+
+/* Q/K normalisation scope: none, or per head (m = d). Inner scope (m = Hq*d) is not built. */
+enum { SA_NORM_NONE = 0, SA_NORM_HEAD = 1 };
+
+/* RoPE pairing: none, split-half pairs (r, r + d/2), interleaved pairs (2r, 2r + 1). */
+enum { SA_ROPE_NONE = 0, SA_ROPE_SPLIT = 1, SA_ROPE_INTERLEAVED = 2 };
+
+/*
+ * qk_norm_rope -- Q/K prologue: per-head RMSNorm, then RoPE, one rounding to bf16.
+ *
+ * Page "flashdreams.accelerated", section "Multi Head Attention Definition": the RMSNorm
+ * equation gamma * z / sqrt(mean(z^2) + eps) with head scope (m = d, each head separately),
+ * followed by the pair rotation [[cos t, -sin t], [sin t, cos t]] with angle t = theta_{p,r};
+ * V is neither normalised nor rotated. With before-cache RoPE the rotated keys are what the
+ * K/V cache stores, so k_out may point straight into a cache (see below).
+ *
+ *   q_in      [B, L, Hq, d] bf16 (device). q_out: [B, L, Hq, d] bf16, batch stride
+ *             q_out_bstride elements (>= L*Hq*d; q_out == q_in is allowed: in place).
+ *   k_in      [B, L, Hkv, d] bf16, or NULL for a query-only prologue (cross-attention).
+ *   k_out     destination of the processed keys, row (b, p, h) at
+ *             k_out + b*k_out_bstride + (p*Hkv + h)*d. To write into a cache
+ *             [B, S, Hkv, d] at token slot s0, pass cache_k + s0*Hkv*d and S*Hkv*d.
+ *             NULL iff k_in is NULL.
+ *   gamma_q, gamma_k  fp32 [d] RMSNorm weights; both NULL iff norm_scope == SA_NORM_NONE
+ *             (gamma_k may be NULL when k_in is NULL).
+ *   rope_angles fp32 [L, d/2] host-built angles theta_{p,r} for the L positions of this chunk
+ *             (device pointer); NULL iff rope_style == SA_ROPE_NONE. The same angles rotate q
+ *             and k (positions are shared by the chunk's queries and keys).
+ *   eps       RMSNorm epsilon (>= 0).
+ * Arithmetic in fp32; the only rounding to bf16 is the final store.
+ * Returns SA_OK, or SA_ERR_* as described at the top of this file.
+ */
+int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride,
+                 const void* k_in, void* k_out, int64_t k_out_bstride,
+                 const float* gamma_q, const float* gamma_k, const float* rope_angles,
+                 int B, int L, int Hq, int Hkv, int d, float eps,
+                 int norm_scope, int rope_style, void* stream);
+
+/*
+ * kv_cache_slot -- rolling sink + window cache: where chunk `chunk_idx` is written and how
+ * many cached tokens the chunk then attends to. Pure host integer function (no device work).
+ *
+ * Page "flashdreams.accelerated", section "Generic Multi Head Attention Interface": the
+ * BlockKVCache storage is [B, sink_size + window_size, H, d]; before_update(chunk_idx) precedes
+ * the attention call and the current chunk is written into the rolling cache before it is
+ * queried. Page "Accelerated building blocks" (section "Cache lifecycle"): chunk, window and
+ * sink sizes are fixed. Slot rule (sizes in tokens, multiples of chunk_len Lc;
+ * n_sink = sink_size/Lc, n_win = window_size/Lc >= 1):
+ *     slot_base(c)   = c*Lc                                   if c < n_sink (sinks stay)
+ *                    = sink_size + ((c - n_sink) mod n_win)*Lc otherwise (window ring)
+ *     visible_len(c) = min((c + 1)*Lc, sink_size + window_size)
+ * Attention over physical slots [0, visible_len) equals attention over the chunks in arrival
+ * order, because non-causal attention does not depend on key order and before-cache RoPE has
+ * already placed the positions in the stored keys.
+ *   slot_base_out, visible_len_out: HOST pointers receiving the results.
+ * Returns SA_OK, SA_ERR_NULL, or SA_ERR_RANGE (negative chunk index, Lc <= 0, sizes not
+ * multiples of Lc, window_size < Lc, or a result that does not fit).
+ */
+int kv_cache_slot(int64_t chunk_idx, int chunk_len, int sink_size, int window_size,
+                  int64_t* slot_base_out, int* visible_len_out);
+
+/*
+ * kv_cache_append -- copy one chunk of keys and/or values into its cache slot range.
+ *
+ * Same page and section as kv_cache_slot ("K/V cache updates" of the streaming attention).
+ *   k_new, v_new   [B, Lc, Hkv, d] 16-bit (device); either may be NULL (skipped), not both.
+ *                  k_new is NULL when qk_norm_rope already wrote the rotated keys.
+ *   cache_k, cache_v  [B, sink_size + window_size, Hkv, d]; a cache whose source is NULL may
+ *                  also be NULL.
+ * Rows [slot_base, slot_base + Lc) of every batch are overwritten (slot_base from
+ * kv_cache_slot); all other rows are untouched. A byte copy: bit-exact.
+ */
+int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                    int B, int Lc, int Hkv, int d, int sink_size, int window_size,
+                    int64_t chunk_idx, void* stream);
+
+/*
+ * attn_forward -- scaled dot-product attention forward pass, bf16 in and out.
+ *
+ * Page "flashdreams.accelerated", section "Multi Head Attention Definition", attention
+ * equation: out_h = softmax(Q_h K_h^T * scale) V_h for every head h (scale = 1/sqrt(d) in
+ * that equation; passed explicitly here). Computed tile by tile with an online softmax, so
+ * the Lq x Lk score matrix is never stored; the result equals the definition up to rounding.
+ *   q, out   [B, Lq, Hq, d] bf16; k, v [B, Lk, Hkv, d] bf16 (all device, contiguous).
+ *   Hq % Hkv == 0: query head h reads key/value head h / (Hq / Hkv) (grouped heads).
+ *   causal   0 or 1. With 1, query i sees key j iff j <= i + (Lk - Lq) (queries aligned to
+ *            the end of the keys); requires Lq <= Lk.
+ *   Lk >= 1; Lq == 0 or B == 0 is a successful no-op. d in {64, 128}.
+ * Accumulation in fp32; probabilities enter the P*V product as fp16 (V converted exactly for
+ * |v| in [2^-17, 65504]); the output is rounded once to bf16.
+ */
+int attn_forward(const void* q, const void* k, const void* v, void* out,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                 float scale, int causal, void* stream);
+
+/* attn_forward_f16 -- the same operation with IEEE binary16 q, k, v and out. */
+int attn_forward_f16(const void* q, const void* k, const void* v, void* out,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                     float scale, int causal, void* stream);
+
+/*
+ * attn_forward_kvstride -- attention over the first Lk tokens of a larger K/V buffer, such as
+ * a rolling cache [B, S, Hkv, d] with S >= Lk (streaming self-attention) or a static context
+ * cache (cross-attention). kv_bstride is the element distance between batches of k and v
+ * (S*Hkv*d for a cache; >= Lk*Hkv*d). dtype is SA_DTYPE_BF16 or SA_DTYPE_F16 for all four
+ * tensors. Otherwise identical to attn_forward.
+ */
+int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out,
+                          int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                          float scale, int causal, int64_t kv_bstride, int dtype, void* stream);
+
+/* Text describing the last non-zero status returned to this thread ("" if none). */
+const char* sa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMATTN_H */

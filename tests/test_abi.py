@@ -1,0 +1,117 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol, validates its
+arguments on the host (no GPU work happens for a rejected call), and its rolling-cache slot rule
+agrees with the oracle's chunk-by-chunk simulation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from head_attention_streaming_amd import binding
+from oracle.cache import RollingCacheModel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamattn.h")
+
+lib = pytest.importorskip("head_attention_streaming_amd.binding").lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    # the exported symbols are C names (no C++ mangling)
+    raw = ctypes.CDLL(binding.library_path())
+    for name in _declared():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def _attn(q=1, k=1, v=1, out=16, B=1, Hq=8, Hkv=8, Lq=16, Lk=16, d=128, scale=0.1, causal=0):
+    # fake but aligned non-null addresses: only reached if validation passes, which these avoid
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    return lib().attn_forward(P(q), P(k), P(v), P(out), B, Hq, Hkv, Lq, Lk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -3), (dict(d=256), -3), (dict(Hq=6, Hkv=4), -2), (dict(causal=1, Lq=20, Lk=16), -2),
+    (dict(causal=2), -5), (dict(Lq=-1), -5), (dict(Hq=0), -5), (dict(scale=0.0), -5),
+    (dict(scale=float("nan")), -5), (dict(Lk=0), -2), (dict(q=None), -1), (dict(v=None), -1),
+])
+def test_attn_forward_rejects_bad_arguments(kw, code):
+    assert _attn(**kw) == code
+    assert lib().sa_last_error().decode() != ""
+
+
+def test_attn_forward_misaligned_pointer():
+    L = lib()
+    st = L.attn_forward(ctypes.c_void_p(4096 + 2), ctypes.c_void_p(8192), ctypes.c_void_p(8192),
+                        ctypes.c_void_p(8192), 1, 1, 1, 4, 4, 64, 0.1, 0, None)
+    assert st == -4
+
+
+def test_attn_forward_empty_is_noop():
+    assert _attn(q=None, k=None, v=None, out=None, Lq=0) == 0
+    assert _attn(q=None, k=None, v=None, out=None, B=0) == 0
+
+
+def test_kvstride_too_small_rejected():
+    L = lib()
+    P = ctypes.c_void_p(4096)
+    assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 99 * 4 * 64, 0, None) == -2
+    assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 100 * 4 * 64, 7, None) == -3
+
+
+def test_qk_norm_rope_rejects_bad_arguments():
+    L = lib()
+    P = ctypes.c_void_p(4096)
+    g = ctypes.c_void_p(8192)
+    # head dim not built
+    assert L.qk_norm_rope(P, P, 96 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 96, 1e-6, 1, 1, None) == -3
+    # inner scope is not built
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 2, 1, None) == -3
+    # RoPE enabled without angles
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, None, 1, 4, 8, 0, 128, 1e-6, 1, 1, None) == -1
+    # head norm without weights
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, None, None, g, 1, 4, 8, 0, 128, 1e-6, 1, 1, None) == -1
+    # k_in without k_out
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, P, None, 0, g, g, g, 1, 4, 8, 8, 128, 1e-6, 1, 1, None) == -1
+    # output batch stride smaller than one batch
+    assert L.qk_norm_rope(P, P, 100, None, None, 0, g, None, g, 2, 4, 8, 0, 128, 1e-6, 1, 1, None) == -2
+
+
+def test_kv_cache_append_rejects_bad_arguments():
+    L = lib()
+    P = ctypes.c_void_p(4096)
+    assert L.kv_cache_append(None, None, P, P, 1, 16, 2, 64, 0, 64, 0, None) == -1
+    assert L.kv_cache_append(None, P, None, None, 1, 16, 2, 64, 0, 64, 0, None) == -1
+    assert L.kv_cache_append(None, P, None, P, 1, 16, 2, 64, 8, 64, 0, None) == -5   # sink not a multiple
+    assert L.kv_cache_append(None, P, None, P, 1, 16, 2, 64, 0, 8, 0, None) == -5    # window < chunk
+    assert L.kv_cache_append(None, P, None, P, 1, 16, 2, 96, 0, 64, 0, None) == -3
+    assert L.kv_cache_append(None, P, None, P, 1, 16, 2, 64, 0, 64, -1, None) == -5
+
+
+@pytest.mark.parametrize("Lc,sink,window", [(1785, 0, 7140), (10, 10, 30), (10, 20, 10), (3, 0, 3), (7, 14, 35)])
+def test_kv_cache_slot_matches_oracle_simulation(Lc, sink, window):
+    model = RollingCacheModel(Lc, sink, window)
+    for c in range(2 * (sink + window) // Lc + 7):
+        expect_slot = model.write(c)
+        slot, vis = binding.kv_cache_slot(c, Lc, sink, window)
+        assert slot == expect_slot, c
+        assert vis == model.visible_len(), c
+
+
+def test_kv_cache_slot_large_chunk_index():
+    slot, vis = binding.kv_cache_slot(10 ** 15, 16, 32, 64)
+    assert vis == 96 and slot == 32 + ((10 ** 15 - 2) % 4) * 16
+    with pytest.raises(binding.StreamAttnError):
+        binding.kv_cache_slot(-1, 16, 0, 64)

@@ -1,0 +1,140 @@
+"""GPU parity of attn_forward / attn_forward_f16 / attn_forward_kvstride against the fp64 oracle.
+
+Sizes span several 128-query and 64-key tiles with ragged tails; the full-size workloads are
+checked on sampled rows (the oracle computes each sampled row exactly over all its keys)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_attention_streaming_amd import binding, synthetic
+from parity import assert_attention_close, sample_rows, widen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(q, k, v, scale, causal, dtype):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty_like(qd)
+    if dtype == "bf16":
+        binding.attn_forward(qd, kd, vd, out, scale, causal)
+    else:
+        binding.attn_forward_f16(qd, kd, vd, out, scale, causal)
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # name, B, Lq, Lk, Hq, Hkv, d, dtype, causal
+    ("noncausal_257_bf16_d128", 1, 257, 257, 8, 8, 128, "bf16", False),
+    ("ragged_gqa_f16_d64", 2, 200, 333, 4, 2, 64, "f16", False),
+    ("causal_square_f16_d64", 2, 190, 190, 3, 3, 64, "f16", True),
+    ("causal_rect_bf16_d128", 1, 100, 300, 2, 2, 128, "bf16", True),
+    ("causal_square_bf16_d128", 1, 300, 300, 2, 2, 128, "bf16", True),
+    ("single_query_single_key", 1, 1, 1, 1, 1, 128, "bf16", False),
+    ("tile_plus_one", 1, 129, 65, 2, 1, 128, "bf16", False),
+    ("tile_minus_one", 1, 127, 63, 2, 2, 64, "bf16", False),
+    ("mqa_bf16_d128", 1, 150, 200, 8, 1, 128, "bf16", False),
+    ("f16_d128", 1, 200, 250, 2, 2, 128, "f16", False),
+    ("bf16_d64_batch", 3, 130, 70, 2, 2, 64, "bf16", False),
+    ("one_key_many_queries", 2, 300, 1, 2, 2, 128, "bf16", False),
+    ("causal_one_row_f16", 1, 1, 97, 2, 2, 64, "f16", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_attention_matches_oracle(case):
+    name, B, Lq, Lk, Hq, Hkv, d, dtype, causal = case
+    print(f"[case] {case}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 10000)
+    scale = d ** -0.5
+    out = _run(q, k, v, scale, causal, dtype)
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           scale, causal)
+    assert_attention_close(out, ref, name)
+
+
+def test_causal_2048_f16_full():
+    """Causal MHA [2, 2048, 8, 64] fp16, scale 1/8: every output element."""
+    w = synthetic.WORKLOADS["causal_2048_f16"]
+    print(f"[case] {w}", flush=True)
+    q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
+    out = _run(q, k, v, w.scale, True, "f16")
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           w.scale, True)
+    assert_attention_close(out, ref, w.name)
+
+
+def test_noncausal_20480_bf16_sampled_rows():
+    """Long non-causal MHA [1, 20480, 56, 128] bf16: 2048+ sampled rows, each over all 20480 keys."""
+    w = synthetic.WORKLOADS["mha_20480_bf16"]
+    print(f"[case] {w}", flush=True)
+    q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
+    out = _run(q, k, v, w.scale, False, "bf16")
+    rows = sample_rows(w.B, w.Lq, w.Hq, 2048, seed=7)
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           w.scale, False, rows=rows)
+    got = out.reshape(-1, w.d)[torch.from_numpy(rows).to(DEV)]
+    assert_attention_close(got, ref, w.name)
+
+
+def test_peaky_softmax():
+    q, k, v = synthetic.attention_inputs(1, 257, 257, 4, 4, 128, "bf16", seed=31, q_scale=8.0)
+    out = _run(q, k, v, 128 ** -0.5, False, "bf16")
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           128 ** -0.5)
+    assert_attention_close(out, ref, "peaky", ulp_floor=True)
+
+
+def test_scores_rising_across_tiles_forces_rescale():
+    # q = 1 on every feature; key j gets + t_j on every feature with t_j rising: the row maximum
+    # moves into every new key tile, so each tile rescales the partial output.
+    B, Lq, Lk, H, d = 1, 130, 517, 2, 128
+    g = torch.Generator().manual_seed(77)
+    q = torch.ones((B, Lq, H, d)).to(torch.bfloat16)
+    t = torch.linspace(0.0, 3.0, Lk).view(1, Lk, 1, 1)
+    k = (0.3 * torch.randn((B, Lk, H, d), generator=g) + t).to(torch.bfloat16)
+    v = torch.randn((B, Lk, H, d), generator=g).to(torch.bfloat16)
+    scale = 0.05
+    out = _run(q, k, v, scale, False, "bf16")
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape), scale)
+    assert_attention_close(out, ref, "rising")
+
+
+def test_maximum_in_last_tile():
+    q, k, v = synthetic.attention_inputs(1, 64, 300, 2, 2, 128, "bf16", seed=5)
+    k[:, 297] = q[:, 10]  # key 297 (last, ragged tile) aligns with query 10: a dominant score
+    k[:, 297] = (k[:, 297].float() * 3).to(torch.bfloat16)
+    out = _run(q, k, v, 128 ** -0.5, False, "bf16")
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           128 ** -0.5)
+    assert_attention_close(out, ref, "max_last_tile")
+
+
+def test_kvstride_reads_prefix_of_larger_buffer():
+    B, Lq, S, Lk, H, d = 2, 140, 400, 333, 3, 128
+    q, k, v = synthetic.attention_inputs(B, Lq, S, H, H, d, "bf16", seed=9)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty_like(qd)
+    binding.attn_forward_kvstride(qd, kd, vd, out, Lk, 0.1, False)
+    torch.cuda.synchronize()
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k[:, :Lk]).reshape(B, Lk, H, d),
+                           widen(v[:, :Lk]).reshape(B, Lk, H, d), 0.1)
+    assert_attention_close(out, ref, "kvstride")
+
+
+def test_deterministic_repeat():
+    q, k, v = synthetic.attention_inputs(1, 333, 1000, 4, 4, 128, "bf16", seed=11)
+    a = _run(q, k, v, 0.09, False, "bf16")
+    b = _run(q, k, v, 0.09, False, "bf16")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_query_is_noop():
+    q = torch.empty((1, 0, 2, 128), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((1, 5, 2, 128), device=DEV).to(torch.bfloat16)
+    binding.attn_forward(q, k, k, torch.empty_like(q), 0.1, False)
+    torch.cuda.synchronize()

@@ -1,0 +1,188 @@
+"""GPU parity of the streaming path: qk_norm_rope (per-head RMSNorm + RoPE), kv_cache_append
+(bit-exact), and streaming self-attention / cross-attention end to end, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from head_attention_streaming_amd import binding, synthetic
+from oracle.cache import RollingCacheModel
+from parity import assert_attention_close, assert_within_one_ulp, sample_rows, widen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SENTINEL = 0x7E11  # a bf16 NaN pattern no copy produces
+
+
+def _oracle_prologue(x, gamma, eps, angles, style):
+    g = None if gamma is None else gamma.double().numpy()
+    a = None if angles is None else angles.double().numpy()
+    return oracle.qk_norm_rope(widen(x).reshape(x.shape), g, eps, a, style)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("style", [binding.SA_ROPE_SPLIT, binding.SA_ROPE_INTERLEAVED, binding.SA_ROPE_NONE])
+@pytest.mark.parametrize("with_k", [True, False])
+def test_qk_norm_rope_matches_oracle(d, style, with_k):
+    B, L, Hq, Hkv = 2, 37, 5, 3
+    print(f"[case] d={d} style={style} with_k={with_k}", flush=True)
+    g = torch.Generator().manual_seed(100 + d + style)
+    q = synthetic.normal((B, L, Hq, d), "bf16", g, 2.0)
+    k = synthetic.normal((B, L, Hkv, d), "bf16", g, 0.5)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    ang = synthetic.rope_angles(np.arange(5000, 5000 + L), d) if style else None
+    qd, kd = q.to(DEV), k.to(DEV)
+    qo = torch.empty_like(qd)
+    ko = torch.empty_like(kd) if with_k else None
+    binding.qk_norm_rope(qd, qo, kd if with_k else None, ko, gq.to(DEV), gk.to(DEV) if with_k else None,
+                         ang.to(DEV) if style else None, 1e-6, binding.SA_NORM_HEAD, style)
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, style), "q")
+    if with_k:
+        assert_within_one_ulp(ko, _oracle_prologue(k, gk, 1e-6, ang, style), "k")
+
+
+def test_qk_norm_rope_without_norm_and_in_place():
+    B, L, H, d = 1, 20, 4, 128
+    g = torch.Generator().manual_seed(3)
+    q = synthetic.normal((B, L, H, d), "bf16", g)
+    ang = synthetic.rope_angles(np.arange(L) * 97, d)
+    qd = q.to(DEV)
+    binding.qk_norm_rope(qd, qd, None, None, None, None, ang.to(DEV), 0.0, binding.SA_NORM_NONE,
+                         binding.SA_ROPE_SPLIT)  # in place, rotation only
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qd, _oracle_prologue(q, None, 0.0, ang, oracle.SPLIT), "rope only")
+
+
+def test_qk_norm_rope_full_streaming_chunk():
+    """Prologue of the streaming workload at full size: [1, 1785, 40, 128] q and k, split RoPE at
+    absolute positions of chunk 5, keys written straight into a 4-chunk cache slot range."""
+    L, H, d, S = 1785, 40, 128, 7140
+    c = 5
+    g = torch.Generator().manual_seed(1300 + c)
+    q = synthetic.normal((1, L, H, d), "bf16", g)
+    k = synthetic.normal((1, L, H, d), "bf16", g)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    ang = synthetic.rope_angles(np.arange(c * L, (c + 1) * L), d)
+    slot, _ = binding.kv_cache_slot(c, L, 0, S)
+    cache = torch.full((1, S, H, d), 0, dtype=torch.int16, device=DEV)
+    cache.fill_(SENTINEL)
+    cache = cache.view(torch.bfloat16)
+    qo = torch.empty((1, L, H, d), dtype=torch.bfloat16, device=DEV)
+    binding.qk_norm_rope(q.to(DEV), qo, k.to(DEV), cache[:, slot:], gq.to(DEV), gk.to(DEV), ang.to(DEV), 1e-6,
+                         binding.SA_NORM_HEAD, binding.SA_ROPE_SPLIT, k_out_bstride=S * H * d)
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, oracle.SPLIT), "q chunk")
+    assert_within_one_ulp(cache[:, slot:slot + L], _oracle_prologue(k, gk, 1e-6, ang, oracle.SPLIT), "k chunk")
+    untouched = torch.cat([cache[:, :slot], cache[:, slot + L:]], dim=1).view(torch.int16)
+    assert bool((untouched == SENTINEL).all())
+
+
+@pytest.mark.parametrize("B,Lc,H,d,sink,window", [(2, 16, 3, 64, 16, 48), (1, 1785, 40, 128, 0, 7140)])
+def test_kv_cache_append_bit_exact_fill_and_eviction(B, Lc, H, d, sink, window):
+    print(f"[case] B={B} Lc={Lc} H={H} d={d} sink={sink} window={window}", flush=True)
+    S = sink + window
+    model = RollingCacheModel(Lc, sink, window)
+    cache_k = torch.full((B, S, H, d), SENTINEL, dtype=torch.int16, device=DEV)
+    cache_v = torch.full((B, S, H, d), SENTINEL, dtype=torch.int16, device=DEV)
+    expect_k = torch.full((B, S, H, d), SENTINEL, dtype=torch.int16)
+    expect_v = torch.full((B, S, H, d), SENTINEL, dtype=torch.int16)
+    n_chunks = 2 * S // Lc + 2
+    g = torch.Generator().manual_seed(55)
+    for c in range(n_chunks):
+        kc = torch.randint(-32768, 32767, (B, Lc, H, d), generator=g, dtype=torch.int16)
+        vc = torch.randint(-32768, 32767, (B, Lc, H, d), generator=g, dtype=torch.int16)
+        s0 = model.write(c)
+        expect_k[:, s0:s0 + Lc] = kc
+        expect_v[:, s0:s0 + Lc] = vc
+        binding.kv_cache_append(kc.to(DEV), vc.to(DEV), cache_k, cache_v, c, sink, window)
+        torch.cuda.synchronize()
+        assert torch.equal(cache_k.cpu(), expect_k), f"K cache differs after chunk {c}"
+        assert torch.equal(cache_v.cpu(), expect_v), f"V cache differs after chunk {c}"
+
+
+def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, style=binding.SA_ROPE_SPLIT):
+    """Run the streaming loop on the GPU and compare every chunk's output with the oracle."""
+    eps, scale = 1e-6, d ** -0.5
+    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV)
+    model = RollingCacheModel(Lc, sink, window)
+    g = torch.Generator().manual_seed(seed0)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    gqd, gkd = gq.to(DEV), gk.to(DEV)
+    kstar, vals = {}, {}
+    results = []
+    for c in range(n_chunks):
+        gc = torch.Generator().manual_seed(seed0 + c)
+        q = synthetic.normal((B, Lc, H, d), "bf16", gc)
+        k = synthetic.normal((B, Lc, H, d), "bf16", gc)
+        v = synthetic.normal((B, Lc, H, d), "bf16", gc)
+        ang = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d)
+        q_buf = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty_like(q_buf)
+        vis_len = binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, gqd, gkd,
+                                                     ang.to(DEV), eps, scale, style)
+        torch.cuda.synchronize()
+        # oracle: prologue in fp64, rounded once to the bf16 the cache stores; logical window
+        qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang, style), "bf16")
+        kstar[c] = oracle.round_to(_oracle_prologue(k, gk, eps, ang, style), "bf16")
+        vals[c] = widen(v).reshape(v.shape)
+        model.write(c)
+        vis = model.visible_chunks()
+        assert vis_len == model.visible_len()
+        K = np.concatenate([kstar[x] for x in vis], axis=1)
+        V = np.concatenate([vals[x] for x in vis], axis=1)
+        if rows_per_chunk is None:
+            ref = oracle.attention(qs, K, V, scale)
+            got = out
+        else:
+            rows = sample_rows(B, Lc, H, rows_per_chunk, seed=c)
+            ref = oracle.attention(qs, K, V, scale, rows=rows)
+            got = out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)]
+        results.append(assert_attention_close(got, ref, f"chunk {c}"))
+        # the cache holds raw V at the model's slot, bit for bit
+        s0 = model.slot_of(c)
+        assert torch.equal(cache.v[:, s0:s0 + Lc].cpu().view(torch.int16), v.view(torch.int16))
+    return results
+
+
+def test_streaming_small_with_sink_full_compare():
+    # sink 1 chunk + window 3 chunks: fill (chunks 0-3) and several evictions (4-8)
+    _streaming_run(B=2, Lc=100, H=4, d=128, sink=100, window=300, n_chunks=9, rows_per_chunk=None, seed0=4000)
+
+
+def test_streaming_interleaved_rope_d64():
+    _streaming_run(B=1, Lc=64, H=3, d=64, sink=0, window=192, n_chunks=5, rows_per_chunk=None, seed0=4100,
+                   style=binding.SA_ROPE_INTERLEAVED)
+
+
+def test_streaming_self_attention_full_size():
+    """Streaming self-attention at full size: chunks of 1785 tokens x 40 heads x 128, rolling cache
+    of 4 chunks (7140 keys), chunks 0-5 (fill, then eviction); sampled rows each chunk."""
+    w = synthetic.WORKLOADS["stream_self_1785x4"]
+    print(f"[case] {w}", flush=True)
+    _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=0, window=w.window, n_chunks=6, rows_per_chunk=512,
+                   seed0=w.seed)
+
+
+def test_cross_attention_full_size():
+    """Cross-attention: B=2, 40 heads, 1785 queries with Q RMSNorm (no RoPE) over a static
+    512-token K/V context; sampled rows."""
+    w = synthetic.WORKLOADS["cross_1785x512"]
+    print(f"[case] {w}", flush=True)
+    g = torch.Generator().manual_seed(w.seed)
+    q = synthetic.normal((w.B, w.Lq, w.Hq, w.d), "bf16", g)
+    k = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g)
+    v = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g)
+    gq = synthetic.norm_weight(w.d, g)
+    qd = q.to(DEV)
+    qs = torch.empty_like(qd)
+    binding.qk_norm_rope(qd, qs, None, None, gq.to(DEV), None, None, 1e-6, binding.SA_NORM_HEAD,
+                         binding.SA_ROPE_NONE)
+    out = torch.empty_like(qd)
+    binding.attn_forward(qs, k.to(DEV), v.to(DEV), out, w.scale, False)
+    torch.cuda.synchronize()
+    q_ref = oracle.round_to(_oracle_prologue(q, gq, 1e-6, None, 0), "bf16")
+    assert_within_one_ulp(qs, _oracle_prologue(q, gq, 1e-6, None, 0), "q norm")
+    rows = sample_rows(w.B, w.Lq, w.Hq, 4096, seed=3)
+    ref = oracle.attention(q_ref, widen(k).reshape(k.shape), widen(v).reshape(v.shape), w.scale, rows=rows)
+    assert_attention_close(out.reshape(-1, w.d)[torch.from_numpy(rows).to(DEV)], ref, w.name)
