@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstreamattn.so")
 SOURCES = ["attn_fwd.hip", "qk_norm_rope.hip", "kv_cache.hip", "capi.hip"]
+# Per-source extra flags. The attention kernel assumes finite inputs (NaN in q/k/v is outside its
+# contract), which lets the compiler fuse the row-maximum tree into v_max3_f32.
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code (hipcc's host pass reports the
@@ -31,7 +34,7 @@ def _hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:

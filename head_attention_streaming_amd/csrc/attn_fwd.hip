@@ -19,6 +19,8 @@
 //   * exp2 with log2(e) folded into the scale; the output is divided by l once at the end.
 // Probabilities use f16 (11-bit significand) for the P*V product; bf16 V is converted to f16
 // when it is staged into LDS (exact for |v| in [2^-17, 65504]).
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -30,6 +32,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes as a native vector
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -61,9 +65,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// 8 bf16 -> 8 f16 (exact in f16's normal range).
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
-    uint4 r;
+// 8 bf16 -> 8 f16 (exact for |v| in [2^-17, 65504]): each bf16 is widened to f32 (the low one
+// by a shift, the high one by clearing the other half) and pairs are packed with RNE.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x) {
+    u32x4 r;
     r.x = pack_f16x2(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u));
     r.y = pack_f16x2(__uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
     r.z = pack_f16x2(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xffff0000u));
@@ -72,13 +77,23 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
 }
 
 template <bool BF16>
-__device__ __forceinline__ f32x16 mfma_qk(uint4 a, uint4 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
     if constexpr (BF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1, so array indices are compile-time
+// constants and the staging arrays stay in registers.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
 }
 
 // max / sum of a value with its copy in the other 32-lane half of the wave
@@ -136,46 +151,69 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
     const int nkt = (kend + kBN - 1) / kBN;
 
     // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of query row q0w + j.
-    uint4 qf[DC];
+    u32x4 qf[DC];
     {
         const int qrow = min(q0w + j, p.Lq - 1);
         const uint16_t* qp = p.q + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D + 8 * g;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const uint4*>(qp + 16 * c);
+        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
     }
 
     const uint16_t* kbase = p.k + b * p.kv_bstride + hk * D;
     const uint16_t* vbase = p.v + b * p.kv_bstride + hk * D;
 
-    uint4 kreg[NCH], vreg[NCH];
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int id = tid + kThreads * u;
-            const int row = id / CPR, col = (id % CPR) * 8;
-            const int key = min(kt * kBN + row, p.Lk - 1);  // tail keys re-read a valid row; masked below
-            const int64_t off = (int64_t)key * p.kv_tstride + col;
-            kreg[u] = *reinterpret_cast<const uint4*>(kbase + off);
-            vreg[u] = *reinterpret_cast<const uint4*>(vbase + off);
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int id = tid + kThreads * u;
-            const int row = id / CPR, col = (id % CPR) * 8;
-            *reinterpret_cast<uint4*>(&Ks[buf][row * KST + col]) = kreg[u];
-            *reinterpret_cast<uint4*>(&Vs[buf][row * VST + col]) = BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
-        }
-    };
+    // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, features
+    // scol..scol+7) of every tile; only the last tile clamps its rows to Lk - 1.
+    constexpr int RSTEP = kThreads / CPR;
+    const int srow0 = tid / CPR, scol = (tid % CPR) * 8;
+    const int64_t row_stride = (int64_t)RSTEP * p.kv_tstride;
+    const int64_t tile_stride = (int64_t)kBN * p.kv_tstride;
+    const uint16_t* kg = kbase + (int64_t)srow0 * p.kv_tstride + scol;
+    const uint16_t* vg = vbase + (int64_t)srow0 * p.kv_tstride + scol;
+    uint16_t* ks_st = &Ks[0][srow0 * KST + scol];
+    uint16_t* vs_st = &Vs[0][srow0 * VST + scol];
+    u32x4 kreg[NCH], vreg[NCH];
+
+#define SA_LOAD_TILE(KT)                                                                       \
+    do {                                                                                       \
+        const int kt_ = (KT);                                                                  \
+        if (kt_ * kBN + kBN <= p.Lk) {                                                         \
+            const uint16_t* kt_k = kg + kt_ * tile_stride;                                     \
+            const uint16_t* kt_v = vg + kt_ * tile_stride;                                     \
+            static_for<NCH>([&](auto u) {                                                      \
+                kreg[u] = *reinterpret_cast<const u32x4*>(kt_k + u * row_stride);              \
+                vreg[u] = *reinterpret_cast<const u32x4*>(kt_v + u * row_stride);              \
+            });                                                                                \
+        } else {                                                                               \
+            static_for<NCH>([&](auto u) {                                                      \
+                const int key = min(kt_ * kBN + srow0 + u * RSTEP, p.Lk - 1);                  \
+                const int64_t off = (int64_t)(key - srow0) * p.kv_tstride;                     \
+                kreg[u] = *reinterpret_cast<const u32x4*>(kg + off);                           \
+                vreg[u] = *reinterpret_cast<const u32x4*>(vg + off);                           \
+            });                                                                                \
+        }                                                                                      \
+    } while (0)
+#define SA_STORE_TILE(BUF)                                                                     \
+    do {                                                                                       \
+        static_for<NCH>([&](auto u) {                                                          \
+            *reinterpret_cast<u32x4*>(ks_st + (BUF) * (kBN * KST) + u * RSTEP * KST) = kreg[u]; \
+            *reinterpret_cast<u32x4*>(vs_st + (BUF) * (kBN * VST) + u * RSTEP * VST) =          \
+                BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];                                     \
+        });                                                                                    \
+    } while (0)
 
     f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    float m_run = -1e30f;  // running max of scaled scores (log2 domain); finite so exp2 never sees inf-inf
-    float l_run = 0.f;     // this lane's share of the running row sum
+    // Running maximum used as the exponent offset (log2 domain). It is raised only when a
+    // tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip the O rescale;
+    // probabilities then stay below 2^kRescaleSlack, well inside f16 range. Finite start value,
+    // so exp2 never sees inf - inf.
+    constexpr float kRescaleSlack = 8.0f;
+    float m_run = -1e30f;
+    float l_run = 0.f;  // this lane's share of the running row sum
 
     const float c = p.c;
     const int qabs = q0w + j;
@@ -183,21 +221,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
     const int wave_klast = p.causal ? min(q0w + 31, p.Lq - 1) + shift : p.Lk - 1;
     const int wave_kfirst_masked = p.causal ? q0w + shift + 1 : p.Lk;  // first key masked for some row
 
+    // LDS read addresses (address space 3, so constant offsets fold into the instructions).
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    lds_u4* kq_lane = (lds_u4*)(&Ks[0][j * KST + 8 * g]);
     // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
     // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
     const int G = lane >> 4, L16 = lane & 15;
     const int vrow_lane = 4 * (G >> 1) + (L16 >> 2);
     const int vcol_lane = 16 * (G & 1) + 4 * (L16 & 3);
+    lds_i16x4* v_lane = (lds_i16x4*)(&Vs[0][vrow_lane * VST + vcol_lane]);
 
     if (nkt > 0) {
-        load_tile(0);
-        store_tile(0);
+        SA_LOAD_TILE(0);
+        SA_STORE_TILE(0);
     }
     __syncthreads();
 
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nkt) load_tile(kt + 1);
+        if (kt + 1 < nkt) SA_LOAD_TILE(kt + 1);
 
         const int k0 = kt * kBN;
         if (k0 <= wave_klast) {
@@ -207,10 +249,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-                const uint16_t* kp = &Ks[buf][(kb * 32 + j) * KST + 8 * g];
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    s[kb] = mfma_qk<BF16>(*reinterpret_cast<const uint4*>(kp + 16 * cc), qf[cc], s[kb]);
+                    s[kb] = mfma_qk<BF16>(kq_lane[(buf * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], s[kb]);
             }
             // ---- mask tail keys and keys beyond the causal diagonal
             if (k0 + kBN > p.Lk || k0 + kBN - 1 >= wave_kfirst_masked) {
@@ -223,33 +264,39 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
                         if (!ok) s[kb][r] = -INFINITY;
                     }
             }
-            // ---- online softmax (log2 domain)
-            float mx = s[0][0];
+            // ---- online softmax (log2 domain): tile row max by a tree of v_max3
+            float mx[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                mx[t] = fmaxf(fmaxf(s[t >> 2][4 * (t & 3)], s[t >> 2][4 * (t & 3) + 1]),
+                              fmaxf(s[t >> 2][4 * (t & 3) + 2], s[t >> 2][4 * (t & 3) + 3]));
+            float tmax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
+                               fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+            tmax = half_swap_max(tmax) * c;
+            if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            }
+            float ps[8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = half_swap_max(mx);
-            const float m_new = fmaxf(m_run, mx * c);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float lsum = 0.f;
+                for (int r = 0; r < 16; ++r)
+                    s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_new));
-                    s[kb][r] = e;
-                    lsum += e;
-                }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            for (int t = 0; t < 8; ++t)
+                ps[t] = (s[t >> 2][4 * (t & 3)] + s[t >> 2][4 * (t & 3) + 1]) +
+                        (s[t >> 2][4 * (t & 3) + 2] + s[t >> 2][4 * (t & 3) + 3]);
+            l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
 
             // ---- P^T operands (f16): registers 8hh..8hh+7 of block kb cover 16 keys
-            uint4 pf[2][2];
+            u32x4 pf[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -264,23 +311,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const int row0 = kb * 32 + 16 * hh + vrow_lane;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const uint16_t* vp = &Vs[buf][row0 * VST + 32 * db + vcol_lane];
-                        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-                        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * VST));
+                        const int off = (buf * kBN * VST + (kb * 32 + 16 * hh) * VST + 32 * db) / 4;
+                        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off);
+                        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off + 2 * VST);
                         const i16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                        const f16x8 a = __builtin_bit_cast(f16x8, a8);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pf[kb][hh]),
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
+                                                                        __builtin_bit_cast(f16x8, pf[kb][hh]),
                                                                         o[db], 0, 0, 0);
                     }
                 }
         }
 
-        if (kt + 1 < nkt) store_tile(buf ^ 1);
+        if (kt + 1 < nkt) SA_STORE_TILE(buf ^ 1);
         __syncthreads();
     }
+#undef SA_LOAD_TILE
+#undef SA_STORE_TILE
 
     // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
     const float l = half_swap_sum(l_run);
@@ -294,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
                 const int dcol = 32 * db + 8 * rg + 4 * g;
                 const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
                 const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
-                uint2 w;
+                u32x2 w;
                 if constexpr (BF16) {
                     w.x = pack_bf16x2(x0, x1);
                     w.y = pack_bf16x2(x2, x3);
@@ -302,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
                     w.x = pack_f16x2(x0, x1);
                     w.y = pack_f16x2(x2, x3);
                 }
-                *reinterpret_cast<uint2*>(op + dcol) = w;
+                *reinterpret_cast<u32x2*>(op + dcol) = w;
             }
     }
 }
