@@ -39,8 +39,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kBN = 64;       // keys per tile
+constexpr int kBM = 128;      // query rows per workgroup (4 waves x 32 rows)
 constexpr int kThreads = 256; // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -106,14 +105,23 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Keys per tile: 32 for d = 128, 64 for d = 64 (keeps a wave's registers within 256 so two
+// workgroups share each CU).
+template <int D>
+constexpr int tile_keys() { return D == 128 ? 32 : 64; }
+
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
+    constexpr int kBN = tile_keys<D>();
+    constexpr int KB = kBN / 32;  // 32-key score blocks per tile
+    constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
     constexpr int KST = D + 8;    // LDS row stride of a K tile (elements): conflict-free b128 reads
     constexpr int VST = D + 32;   // LDS row stride of a V tile: conflict-free transposed reads
     constexpr int DC = D / 16;    // QK MFMAs per 32-key block (16 features each)
     constexpr int DB = D / 32;    // 32-feature blocks of the O^T accumulator
     constexpr int CPR = D / 8;    // 16-byte chunks per key row
     constexpr int NCH = kBN * CPR / kThreads;  // 16-byte chunks each thread stages per tile
+    constexpr int RSTEP = kThreads / CPR;      // key rows between a thread's chunks
     static_assert(NCH * kThreads == kBN * CPR, "tile must split evenly over the workgroup");
 
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KST];
@@ -140,86 +148,56 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
     const int hk = h / p.group;
 
     const int qb0 = qblk * kBM;
-    const int q0w = qb0 + wave * 32;
-    const int shift = p.Lk - p.Lq;  // causal: query i sees keys j <= i + shift
+    const int r0 = qb0 + wave * 32;  // this wave's first query row
+    const int qrow = r0 + j;
+    const int shift = p.Lk - p.Lq;   // causal: query i sees keys j <= i + shift
 
     int kend = p.Lk;
-    if (p.causal) {
-        const int qlast = min(qb0 + kBM, p.Lq) - 1;
-        kend = min(p.Lk, qlast + shift + 1);
-    }
+    if (p.causal) kend = min(p.Lk, min(qb0 + kBM, p.Lq) - 1 + shift + 1);
     const int nkt = (kend + kBN - 1) / kBN;
+    // first tile that needs a mask for some row of the workgroup (tail keys or causal diagonal)
+    int t_mask = p.Lk / kBN;
+    if (p.causal) t_mask = min(t_mask, max(0, (qb0 + shift + 1) / kBN));
 
-    // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of query row q0w + j.
+    // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row.
     u32x4 qf[DC];
     {
-        const int qrow = min(q0w + j, p.Lq - 1);
-        const uint16_t* qp = p.q + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D + 8 * g;
+        const uint16_t* qp = p.q + b * p.q_bstride + (int64_t)min(qrow, p.Lq - 1) * p.q_tstride + h * D + 8 * g;
 #pragma unroll
         for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
     }
 
-    const uint16_t* kbase = p.k + b * p.kv_bstride + hk * D;
-    const uint16_t* vbase = p.v + b * p.kv_bstride + hk * D;
-
     // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, features
-    // scol..scol+7) of every tile; only the last tile clamps its rows to Lk - 1.
-    constexpr int RSTEP = kThreads / CPR;
+    // scol..scol+7) of every tile; rows past Lk re-read row Lk - 1 (their scores are masked).
     const int srow0 = tid / CPR, scol = (tid % CPR) * 8;
-    const int64_t row_stride = (int64_t)RSTEP * p.kv_tstride;
-    const int64_t tile_stride = (int64_t)kBN * p.kv_tstride;
-    const uint16_t* kg = kbase + (int64_t)srow0 * p.kv_tstride + scol;
-    const uint16_t* vg = vbase + (int64_t)srow0 * p.kv_tstride + scol;
+    const uint16_t* kg = p.k + b * p.kv_bstride + hk * D + scol;
+    const uint16_t* vg = p.v + b * p.kv_bstride + hk * D + scol;
     uint16_t* ks_st = &Ks[0][srow0 * KST + scol];
     uint16_t* vs_st = &Vs[0][srow0 * VST + scol];
     u32x4 kreg[NCH], vreg[NCH];
-
-#define SA_LOAD_TILE(KT)                                                                       \
-    do {                                                                                       \
-        const int kt_ = (KT);                                                                  \
-        if (kt_ * kBN + kBN <= p.Lk) {                                                         \
-            const uint16_t* kt_k = kg + kt_ * tile_stride;                                     \
-            const uint16_t* kt_v = vg + kt_ * tile_stride;                                     \
-            static_for<NCH>([&](auto u) {                                                      \
-                kreg[u] = *reinterpret_cast<const u32x4*>(kt_k + u * row_stride);              \
-                vreg[u] = *reinterpret_cast<const u32x4*>(kt_v + u * row_stride);              \
-            });                                                                                \
-        } else {                                                                               \
-            static_for<NCH>([&](auto u) {                                                      \
-                const int key = min(kt_ * kBN + srow0 + u * RSTEP, p.Lk - 1);                  \
-                const int64_t off = (int64_t)(key - srow0) * p.kv_tstride;                     \
-                kreg[u] = *reinterpret_cast<const u32x4*>(kg + off);                           \
-                vreg[u] = *reinterpret_cast<const u32x4*>(vg + off);                           \
-            });                                                                                \
-        }                                                                                      \
-    } while (0)
-#define SA_STORE_TILE(BUF)                                                                     \
-    do {                                                                                       \
-        static_for<NCH>([&](auto u) {                                                          \
-            *reinterpret_cast<u32x4*>(ks_st + (BUF) * (kBN * KST) + u * RSTEP * KST) = kreg[u]; \
-            *reinterpret_cast<u32x4*>(vs_st + (BUF) * (kBN * VST) + u * RSTEP * VST) =          \
-                BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];                                     \
-        });                                                                                    \
-    } while (0)
-
-    f32x16 o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    // Running maximum used as the exponent offset (log2 domain). It is raised only when a
-    // tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip the O rescale;
-    // probabilities then stay below 2^kRescaleSlack, well inside f16 range. Finite start value,
-    // so exp2 never sees inf - inf.
-    constexpr float kRescaleSlack = 8.0f;
-    float m_run = -1e30f;
-    float l_run = 0.f;  // this lane's share of the running row sum
-
-    const float c = p.c;
-    const int qabs = q0w + j;
-    // last key any row of this wave may see; tiles past it hold no visible key for this wave
-    const int wave_klast = p.causal ? min(q0w + 31, p.Lq - 1) + shift : p.Lk - 1;
-    const int wave_kfirst_masked = p.causal ? q0w + shift + 1 : p.Lk;  // first key masked for some row
+    auto load_k = [&](int kt) __attribute__((always_inline)) {
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
+            kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * p.kv_tstride);
+        });
+    };
+    auto load_v = [&](int kt) __attribute__((always_inline)) {
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
+            vreg[u] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * p.kv_tstride);
+        });
+    };
+    auto store_k = [&](int slot) __attribute__((always_inline)) {
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x4*>(ks_st + slot * (kBN * KST) + u * RSTEP * KST) = kreg[u];
+        });
+    };
+    auto store_v = [&](int slot) __attribute__((always_inline)) {
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x4*>(vs_st + slot * (kBN * VST) + u * RSTEP * VST) =
+                BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+        });
+    };
 
     // LDS read addresses (address space 3, so constant offsets fold into the instructions).
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
@@ -227,52 +205,105 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
     // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
     // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
     const int G = lane >> 4, L16 = lane & 15;
-    const int vrow_lane = 4 * (G >> 1) + (L16 >> 2);
-    const int vcol_lane = 16 * (G & 1) + 4 * (L16 & 3);
-    lds_i16x4* v_lane = (lds_i16x4*)(&Vs[0][vrow_lane * VST + vcol_lane]);
+    lds_i16x4* v_lane = (lds_i16x4*)(&Vs[0][(4 * (G >> 1) + (L16 >> 2)) * VST + 16 * (G & 1) + 4 * (L16 & 3)]);
 
-    if (nkt > 0) {
-        SA_LOAD_TILE(0);
-        SA_STORE_TILE(0);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) SA_LOAD_TILE(kt + 1);
-
-        const int k0 = kt * kBN;
-        if (k0 <= wave_klast) {
-            // ---- S^T = K Q^T : two 32-key blocks
-            f32x16 s[2];
+    const float c = p.c;
+    // Running maximum used as the exponent offset (log2 domain). It is raised only when a
+    // tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip the O rescale;
+    // probabilities then stay below 2^kRescaleSlack, well inside f16 range. Finite start value,
+    // so exp2 never sees inf - inf.
+    constexpr float kRescaleSlack = 8.0f;
+    float m_run = -1e30f;
+    float l_run = 0.f;  // this lane's share of the row sum (its own keys)
+    f32x16 o[DB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    f32x16 s0[KB], s1[KB];  // scores of tile t live in s[t & 1]
+    u32x4 pf[KC];           // f16 probabilities of the previous tile (P^T operands)
+
+    // One pipeline step t:  S(t) = K(t) Q^T  ||  P(t-1) = exp2(S(t-1) c - m)  [MFMA || VALU]
+    //                       O += V(t-1) P(t-1)  ||  stage K(t+1), V(t); row max of S(t)
+    // K(t) and V(t) live in LDS slot t%2; step t overwrites the slots step t-1 read, and the
+    // barrier closing each step orders those writes before the next step's reads.
+    auto step = [&](auto do_qk, auto do_pv, auto do_mask, int t, f32x16 (&sc)[KB], f32x16 (&sp)[KB]) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value, MASK = decltype(do_mask)::value;
+        if constexpr (QK) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
                 for (int cc = 0; cc < DC; ++cc)
-                    s[kb] = mfma_qk<BF16>(kq_lane[(buf * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], s[kb]);
+                    sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
             }
-            // ---- mask tail keys and keys beyond the causal diagonal
-            if (k0 + kBN > p.Lk || k0 + kBN - 1 >= wave_kfirst_masked) {
+        }
+        if constexpr (PV) {
+            // P(t-1) as f16 operands; the row sum adds the f16 values the product uses
+            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+            for (int kc = 0; kc < KC; ++kc) {
+                const int kb = kc >> 1, hh = kc & 1;
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e], c, -m_run));
+                    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e + 1], c, -m_run));
+                    w[e] = pack_f16x2(x0, x1);
+                    if (e & 1)
+                        acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc1, false);
+                    else
+                        acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc0, false);
+                }
+                pf[kc] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+            l_run += acc0 + acc1;
+        }
+        if constexpr (QK) {
+            store_k((t + 1) & 1);  // K(t+1) (slot content unused when t + 1 == nkt)
+            store_v(t & 1);        // V(t)
+            load_k(min(t + 2, nkt - 1));
+            load_v(min(t + 1, nkt - 1));
+        }
+        if constexpr (PV) {
+            const int slot = (t - 1) & 1;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int off = (slot * kBN * VST + 16 * kc * VST + 32 * db) / 4;
+                    const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off);
+                    const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off + 2 * VST);
+                    const i16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
+                                                                    __builtin_bit_cast(f16x8, pf[kc]), o[db], 0, 0, 0);
+                }
+        }
+        if constexpr (QK) {
+            const int k0 = t * kBN;
+            if constexpr (MASK) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const bool ok = key < p.Lk && (!p.causal || key <= qabs + shift);
-                        if (!ok) s[kb][r] = -INFINITY;
+                        const bool ok = key < p.Lk && (!p.causal || key <= qrow + shift);
+                        if (!ok) sc[kb][r] = -INFINITY;
                     }
             }
-            // ---- online softmax (log2 domain): tile row max by a tree of v_max3
-            float mx[8];
+            float mk[KB];
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                mx[t] = fmaxf(fmaxf(s[t >> 2][4 * (t & 3)], s[t >> 2][4 * (t & 3) + 1]),
-                              fmaxf(s[t >> 2][4 * (t & 3) + 2], s[t >> 2][4 * (t & 3) + 3]));
-            float tmax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
-                               fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
-            tmax = half_swap_max(tmax) * c;
+            for (int kb = 0; kb < KB; ++kb) {
+                mk[kb] = fmaxf(sc[kb][0], sc[kb][1]);
+#pragma unroll
+                for (int r = 2; r < 16; r += 2) mk[kb] = fmaxf(fmaxf(mk[kb], sc[kb][r]), sc[kb][r + 1]);
+            }
+            float mloc = mk[0];
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) mloc = fmaxf(mloc, mk[kb]);
+            const float tmax = half_swap_max(mloc) * c;
             if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) {
                 const float m_new = fmaxf(m_run, tmax);
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -283,58 +314,42 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
             }
-            float ps[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                ps[t] = (s[t >> 2][4 * (t & 3)] + s[t >> 2][4 * (t & 3) + 1]) +
-                        (s[t >> 2][4 * (t & 3) + 2] + s[t >> 2][4 * (t & 3) + 3]);
-            l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-
-            // ---- P^T operands (f16): registers 8hh..8hh+7 of block kb cover 16 keys
-            u32x4 pf[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    pf[kb][hh].x = pack_f16x2(s[kb][8 * hh + 0], s[kb][8 * hh + 1]);
-                    pf[kb][hh].y = pack_f16x2(s[kb][8 * hh + 2], s[kb][8 * hh + 3]);
-                    pf[kb][hh].z = pack_f16x2(s[kb][8 * hh + 4], s[kb][8 * hh + 5]);
-                    pf[kb][hh].w = pack_f16x2(s[kb][8 * hh + 6], s[kb][8 * hh + 7]);
-                }
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int off = (buf * kBN * VST + (kb * 32 + 16 * hh) * VST + 32 * db) / 4;
-                        const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off);
-                        const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off + 2 * VST);
-                        const i16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
-                                                                        __builtin_bit_cast(f16x8, pf[kb][hh]),
-                                                                        o[db], 0, 0, 0);
-                    }
-                }
         }
-
-        if (kt + 1 < nkt) SA_STORE_TILE(buf ^ 1);
         __syncthreads();
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // steps 1 .. nkt-1 with both halves; S(t) in s0 for even t, s1 for odd t
+    auto middle = [&](auto do_mask, int t0, int t1) __attribute__((always_inline)) {
+        int t = t0;
+        if (t < t1 && (t & 1)) step(T_{}, T_{}, do_mask, t++, s1, s0);
+        for (; t + 1 < t1; t += 2) {
+            step(T_{}, T_{}, do_mask, t, s0, s1);
+            step(T_{}, T_{}, do_mask, t + 1, s1, s0);
+        }
+        if (t < t1) step(T_{}, T_{}, do_mask, t, s0, s1);
+    };
+
+    if (nkt > 0) {
+        load_k(0);
+        store_k(0);
+        load_k(min(1, nkt - 1));
+        load_v(0);
+        __syncthreads();
+        if (t_mask == 0) step(T_{}, F_{}, T_{}, 0, s0, s1);
+        else step(T_{}, F_{}, F_{}, 0, s0, s1);
+        const int tm = max(1, min(t_mask, nkt));
+        middle(F_{}, 1, tm);
+        middle(T_{}, tm, nkt);
+        if (nkt & 1) step(F_{}, T_{}, F_{}, nkt, s1, s0);  // S(nkt-1) in s0 when nkt-1 is even
+        else step(F_{}, T_{}, F_{}, nkt, s0, s1);
     }
-#undef SA_LOAD_TILE
-#undef SA_STORE_TILE
 
     // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
     const float l = half_swap_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qabs < p.Lq) {
-        uint16_t* op = p.out + b * p.q_bstride + (int64_t)qabs * p.q_tstride + h * D;
+    if (qrow < p.Lq) {
+        uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
