@@ -39,8 +39,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;      // query rows per workgroup (4 waves x 32 rows)
-constexpr int kThreads = 256; // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct KParams {
@@ -105,14 +103,20 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Keys per tile: 32 for d = 128, 64 for d = 64 (keeps a wave's registers within 256 so two
-// workgroups share each CU).
-template <int D>
-constexpr int tile_keys() { return D == 128 ? 32 : 64; }
+// Launch shapes. Every wave owns 32 query rows and every lane stays within 256 registers, so
+// two waves share each SIMD:
+//   NW = 8 waves (256 query rows) per workgroup, one workgroup per CU, 64-key tiles: K/V tiles
+//     are staged once for 256 rows, so each thread converts and stores half as much;
+//   NW = 4 waves (128 rows), two workgroups per CU: twice as many workgroups, for grids that
+//     would otherwise leave CUs idle. Keys per tile: 32 for d = 128, 64 for d = 64.
+template <int D, int NW>
+constexpr int tile_keys() { return (NW == 4 && D == 128) ? 32 : 64; }
 
-template <int D, bool BF16>
-__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
-    constexpr int kBN = tile_keys<D>();
+template <int D, bool BF16, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
+    constexpr int kThreads = NW * 64;
+    constexpr int kBM = NW * 32;  // query rows per workgroup
+    constexpr int kBN = tile_keys<D, NW>();
     constexpr int KB = kBN / 32;  // 32-key score blocks per tile
     constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
     constexpr int KST = D + 8;    // LDS row stride of a K tile (elements): conflict-free b128 reads
@@ -370,8 +374,23 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(KParams p) {
     }
 }
 
-template <int D, bool BF16>
+int device_cu_count() {
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+template <int D, bool BF16, int NW>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+    constexpr int kBM = NW * 32;
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -391,16 +410,26 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     const int64_t nblocks = (int64_t)p.n_qblk * a.Hq * a.B;
     p.nblocks = (int)nblocks;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
+    // 256-row workgroups when there are at least four per CU (long sequences); 128-row ones
+    // otherwise, where twice as many workgroups fill the CUs better (measured on MI355X: the
+    // 40-head, 1785-query workloads run faster with 128 rows, 56 heads x 20480 with 256).
+    const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
+    if (wg256 >= 4 * (int64_t)device_cu_count()) return launch<D, BF16, 8>(a, stream);
+    return launch<D, BF16, 4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     const bool bf16 = a.dtype == 0;
-    if (a.d == 128) return bf16 ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-    return bf16 ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    if (a.d == 128) return bf16 ? launch_shape<128, true>(a, stream) : launch_shape<128, false>(a, stream);
+    return bf16 ? launch_shape<64, true>(a, stream) : launch_shape<64, false>(a, stream);
 }
 
 }  // namespace sa

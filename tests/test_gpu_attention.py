@@ -138,3 +138,23 @@ def test_empty_query_is_noop():
     k = torch.randn((1, 5, 2, 128), device=DEV).to(torch.bfloat16)
     binding.attn_forward(q, k, k, torch.empty_like(q), 0.1, False)
     torch.cuda.synchronize()
+
+
+WIDE_CASES = [
+    # enough (batch, head, 256-row block) workgroups to select the 8-wave launch shape
+    ("wide_ragged_bf16_d128", 1, 4000, 333, 64, 64, 128, "bf16", False),
+    ("wide_causal_f16_d64", 2, 2000, 2000, 64, 64, 64, "f16", True),
+    ("wide_gqa_causal_bf16_d128", 4, 1000, 1100, 64, 8, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_attention_wide_grid_sampled_rows(case):
+    name, B, Lq, Lk, Hq, Hkv, d, dtype, causal = case
+    print(f"[case] {case}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 10000)
+    out = _run(q, k, v, d ** -0.5, causal, dtype)
+    rows = sample_rows(B, Lq, Hq, 3000, seed=11)
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           d ** -0.5, causal, rows=rows)
+    assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name)
