@@ -134,6 +134,27 @@ def make_workload(name: str, dev: str):
 
     def kern():
         binding.attn_forward_kvstride(q_buf, cache.k, cache.v, out, S, w.scale, False)
+
+    # the HBM-bound steps alone, on rotating input sets (each set is read once per 6 calls)
+    rot = {"i": 0}
+    slot = cache.slot_base
+
+    def prologue():
+        q, k, _ = sets[rot["i"] % nsets]
+        rot["i"] += 1
+        binding.qk_norm_rope(q, q_buf, k, cache.k[:, slot:], gq, gk, angles[0], 1e-6, binding.SA_NORM_HEAD,
+                             binding.SA_ROPE_SPLIT, k_out_bstride=S * w.Hkv * w.d)
+
+    def append():
+        _, _, v = sets[rot["i"] % nsets]
+        rot["i"] += 1
+        binding.kv_cache_append(None, v, None, cache.v, state["c"], 0, S)
+
+    elem = 2 * w.B * Lc * w.Hq * w.d  # bytes of one [B, Lc, H, d] bf16 tensor
+    info["hbm_steps"] = {
+        "qk_norm_rope": (prologue, 4 * elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4),  # q,k read + written, angles, gammas
+        "kv_cache_append": (append, 2 * elem),                                   # v read + written
+    }
     info["step"] = "qk_norm_rope(Q,K->cache) + kv_cache_append(V) + attn_forward_kvstride, cache full"
     info["cache_tokens"] = S
     return w, step, kern, info, None
@@ -221,6 +242,14 @@ def main():
         return
     ms_step, wall_ms = time_loop(step, args.steps, args.warmup)
     ms_kern, _ = time_loop(kern, args.steps, 2) if kern is not step else (ms_step, wall_ms)
+
+    hbm = {}
+    for name, (fn, nbytes) in info.pop("hbm_steps", {}).items():
+        ms_h, _ = time_loop(fn, args.steps, args.warmup)
+        hbm[name] = {"us": round(ms_h * 1e3, 2), "bytes": nbytes, "GB/s": round(nbytes / (ms_h * 1e-3) / 1e9, 1),
+                     "frac_of_8TB/s": round(nbytes / (ms_h * 1e-3) / 1e9 / PEAK_HBM, 3)}
+    if hbm:
+        info["hbm_kernels"] = hbm
 
     flops = w.flops
     value = flops / (ms_step * 1e-3) / 1e12

@@ -197,7 +197,8 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
         return fail(SA_ERR_SHAPE, "qk_norm_rope: weights given with norm scope none");
     if ((rope_style != SA_ROPE_NONE) != (rope_angles != nullptr))
         return fail(SA_ERR_NULL, "qk_norm_rope: angles must be given iff RoPE is enabled");
-    for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out})
+    for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out, (const void*)gamma_q,
+                          (const void*)gamma_k})
         if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "qk_norm_rope: pointers must be 16-byte aligned");
     const int64_t nq = mul4(1, L, Hq, d);
     if (nq < 0 || mul4(B, L, k_in ? Hkv : 1, d) < 0) return fail(SA_ERR_RANGE, "qk_norm_rope: tensor too large");

@@ -12,17 +12,18 @@ constexpr int kThreads = 256;
 constexpr int kVecPerThread = 4;
 
 __global__ void __launch_bounds__(kThreads) copy_rows_kernel(CopyArgs a, int64_t nvec_per_batch) {
-    const uint4* src = static_cast<const uint4*>(a.src);
-    uint4* dst = static_cast<uint4*>(a.dst);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* src = static_cast<const u32x4*>(a.src);
+    u32x4* dst = static_cast<u32x4*>(a.dst);
     const int b = blockIdx.y;
     const int64_t dst0 = (b * a.dst_bstride + a.dst_offset) / 8;  // in 16-byte vectors
     const int64_t src0 = b * nvec_per_batch;
     const int64_t base = (int64_t)blockIdx.x * kThreads * kVecPerThread + threadIdx.x;
-    uint4 r[kVecPerThread];
+    u32x4 r[kVecPerThread];
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
         const int64_t i = base + (int64_t)u * kThreads;
-        if (i < nvec_per_batch) r[u] = src[src0 + i];
+        if (i < nvec_per_batch) r[u] = __builtin_nontemporal_load(src + src0 + i);  // read once
     }
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {

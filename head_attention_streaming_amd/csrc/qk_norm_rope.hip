@@ -15,16 +15,41 @@
 namespace sa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 32 head rows per pass for d = 128, so a token's Q and K rows load in one batch
 
+// Cross-lane moves inside a 16-lane DPP row (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadReverse = 0x1B;    // quad_perm [3,2,1,0]
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i of its 16-lane row
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i of its 8-lane half row
+constexpr int kRowRotate8 = 0x128;    // lane i <- lane (i + 8) mod 16 of its row, i.e. i ^ 8
+
+// Sum over the LPR (8 or 16) lanes holding one head row; every lane gets the total.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m);
+    x += dpp<kQuadXor1>(x);
+    x += dpp<kQuadXor2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    if constexpr (LPR == 16) x += dpp<kRowMirror>(x);
     return x;
 }
 
-__device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
+// Value held by the lane whose feature slice is half a head away (lane ^ LPR/2 within the group).
+template <int LPR>
+__device__ __forceinline__ float split_partner(float x) {
+    if constexpr (LPR == 16) return dpp<kRowRotate8>(x);                      // i ^ 8 within 16 lanes
+    else return dpp<kQuadReverse>(dpp<kRowHalfMirror>(x));                    // i ^ 4 within 8 lanes
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void unpack_bf16x8(u32x4 w, float* f) {
     const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -36,18 +61,18 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
     uint32_t a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         f32x2 v = {f[2 * i], f[2 * i + 1]};
         a[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
     }
-    return make_uint4(a[0], a[1], a[2], a[3]);
+    return u32x4{a[0], a[1], a[2], a[3]};
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads) qk_norm_rope_kernel(NormRopeArgs a) {
+__global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs a) {
     constexpr int LPR = D / 8;            // lanes per head row
     constexpr int RPP = kThreads / LPR;   // head rows per pass
     constexpr int HALF = D / 2;
@@ -59,6 +84,31 @@ __global__ void __launch_bounds__(kThreads) qk_norm_rope_kernel(NormRopeArgs a) 
     const int li = tid % LPR;             // which 8-feature slice of the row
     const int rs = tid / LPR;             // row slot within a pass
     const int f0 = 8 * li;
+
+    const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
+    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + ((int64_t)b * a.L + p) * a.Hq * D;
+    const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
+    uint16_t* qout = static_cast<uint16_t*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
+    uint16_t* kout = a.k_out ? static_cast<uint16_t*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
+
+    // Rows are handled NB passes at a time: all NB loads are issued before any is used, so each
+    // thread keeps NB 16-byte reads in flight. rows_padded keeps every lane of a row group in
+    // the loop (the shuffles need all of them); lanes past the last row compute on zeros.
+    constexpr int NB = 4;
+    const int rows_padded = (rows + RPP - 1) / RPP * RPP;
+    u32x4 raw[NB];
+    auto load_batch = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = base + rs + nb * RPP;
+            raw[nb] = u32x4{0u, 0u, 0u, 0u};
+            if (row < rows) {
+                const uint16_t* src = row < a.Hq ? qin + row * D : kin + (row - a.Hq) * D;
+                raw[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + f0));
+            }
+        }
+    };
+    load_batch(0);  // in flight while the angles are turned into cos/sin
 
     if (a.rope_style != 0) {
         for (int r = tid; r < HALF; r += kThreads) {
@@ -88,62 +138,69 @@ __global__ void __launch_bounds__(kThreads) qk_norm_rope_kernel(NormRopeArgs a) 
 
     float gq[8], gk[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        gq[e] = a.norm_scope ? a.gamma_q[f0 + e] : 1.f;
-        gk[e] = (a.norm_scope && a.k_in) ? a.gamma_k[f0 + e] : 1.f;
-    }
-
-    const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
-    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + ((int64_t)b * a.L + p) * a.Hq * D;
-    const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
-    uint16_t* qout = static_cast<uint16_t*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
-    uint16_t* kout = a.k_out ? static_cast<uint16_t*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
-
-    // rows_padded keeps every lane of a row group inside the loop (shuffles need all of them)
-    const int rows_padded = (rows + RPP - 1) / RPP * RPP;
-    for (int row = rs; row < rows_padded; row += RPP) {
-        const bool valid = row < rows;
-        const bool is_q = row < a.Hq;
-        float z[8];
-        if (valid) {
-            const uint16_t* src = is_q ? qin + row * D : kin + (row - a.Hq) * D;
-            unpack_bf16x8(*reinterpret_cast<const uint4*>(src + f0), z);
-        } else {
+    for (int e = 0; e < 8; ++e) gq[e] = gk[e] = 1.f;
+    if (a.norm_scope) {  // uniform: two 16-byte loads per weight vector
+        const f32x4* pq = reinterpret_cast<const f32x4*>(a.gamma_q + f0);
+        const f32x4 q0 = pq[0], q1 = pq[1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+            gq[e] = q0[e];
+            gq[e + 4] = q1[e];
         }
-        if (a.norm_scope) {
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
-            ss = group_sum<LPR>(ss);
-            const float r = 1.f / sqrtf(ss / (float)D + a.eps);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
-        }
-        float o[8];
-        if (a.rope_style == 1) {
-            const bool first = li < LPR / 2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float other = __shfl_xor(z[e], LPR / 2);
-                o[e] = first ? c8[e] * z[e] - s8[e] * other : s8[e] * other + c8[e] * z[e];
-            }
-        } else if (a.rope_style == 2) {
+        if (a.k_in) {
+            const f32x4* pk = reinterpret_cast<const f32x4*>(a.gamma_k + f0);
+            const f32x4 k0 = pk[0], k1 = pk[1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float x0 = z[2 * e], x1 = z[2 * e + 1];
-                o[2 * e] = c8[e] * x0 - s8[e] * x1;
-                o[2 * e + 1] = s8[e] * x0 + c8[e] * x1;
+                gk[e] = k0[e];
+                gk[e + 4] = k1[e];
             }
-        } else {
+        }
+    }
+
+    for (int base = 0; base < rows_padded; base += NB * RPP) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = z[e];
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = base + rs + nb * RPP;
+            if (base + nb * RPP >= rows_padded) break;  // uniform: past the last pass
+            const bool valid = row < rows;
+            const bool is_q = row < a.Hq;
+            float z[8];
+            unpack_bf16x8(raw[nb], z);
+            if (a.norm_scope) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
+                ss = group_sum<LPR>(ss);
+                const float r = 1.f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
+            }
+            float o[8];
+            if (a.rope_style == 1) {
+                const bool first = li < LPR / 2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float other = split_partner<LPR>(z[e]);
+                    o[e] = first ? c8[e] * z[e] - s8[e] * other : s8[e] * other + c8[e] * z[e];
+                }
+            } else if (a.rope_style == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = z[2 * e], x1 = z[2 * e + 1];
+                    o[2 * e] = c8[e] * x0 - s8[e] * x1;
+                    o[2 * e + 1] = s8[e] * x0 + c8[e] * x1;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = z[e];
+            }
+            if (valid) {
+                uint16_t* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
+                *reinterpret_cast<u32x4*>(dst + f0) = pack_bf16x8(o);
+            }
         }
-        if (valid) {
-            uint16_t* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
-            *reinterpret_cast<uint4*>(dst + f0) = pack_bf16x8(o);
-        }
+        if (base + NB * RPP < rows_padded) load_batch(base + NB * RPP);
     }
 }
 
