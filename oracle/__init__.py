@@ -14,7 +14,9 @@ section "Multi Head Attention Definition", unless stated otherwise:
 * ``qk_norm_rope``-- normalisation first, then RoPE (the order the same section uses).
 * ``attention``   -- the scaled dot-product equation A_h = softmax(Q_h K_h^T * scale) V_h.
                      Grouped heads: query head h reads key/value head h // (Hq // Hkv).
-                     Causal: key j visible to query i iff j <= i + Lk - Lq.
+                     Causal: key j visible to query i iff j <= i + Lk - Lq. Local window
+                     (left, right) around i + Lk - Lq, the ``window_size`` of the page
+                     "optimizing-attention-flash" (section "Step 3: Enable advanced features").
 * ``round_to``    -- round-to-nearest-even into bfloat16 / IEEE binary16, from the formats'
                      definitions, applied once to an fp64 value.
 * ``cache``       -- the rolling sink + window K/V cache of the page's "Generic Multi Head
@@ -65,7 +67,7 @@ def _load():
         lib.oracle_decode_f16.argtypes = [P, P, I64]
         lib.oracle_rmsnorm.argtypes = [P, P, P, I64, I, D]
         lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I]
-        lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I, I]
+        lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I]
         lib.oracle_attention.restype = I
         _lib = lib
     return _lib
@@ -167,13 +169,20 @@ def qk_norm_rope(z: np.ndarray, gamma: np.ndarray | None, eps: float, angles: np
 # ------------------------------------------------------------------ attention
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
-              rows: np.ndarray | None = None, nthreads: int | None = None) -> np.ndarray:
+              rows: np.ndarray | None = None, nthreads: int | None = None,
+              window: tuple[int, int] | None = None) -> np.ndarray:
     """softmax(Q K^T * scale) V in fp64.
 
     q: [B, Lq, Hq, d]; k, v: [B, Lk, Hkv, d] (float64 or anything convertible).
     rows: optional flat indices into [B, Lq, Hq]; then the result is [len(rows), d],
     otherwise [B, Lq, Hq, d].
+    window: (left, right) local-attention band around each query's key position i + Lk - Lq
+    (a negative bound is unbounded; the skill page's ``window_size=(left, right)``). causal=True
+    is the band (-1, 0); giving both is an error.
     """
+    if window is not None and causal:
+        raise ValueError("give either causal or window")
+    win_left, win_right = window if window is not None else ((-1, 0) if causal else (-1, -1))
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
@@ -191,7 +200,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
     out = np.empty((nrows, d), dtype=np.float64)
     rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                   None if rows_arr is None else _ptr(rows_arr), nrows,
-                                  B, Hq, Hkv, Lq, Lk, d, float(scale), int(bool(causal)),
+                                  B, Hq, Hkv, Lq, Lk, d, float(scale), int(win_left), int(win_right),
                                   nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle_attention failed")

@@ -105,14 +105,16 @@ typedef struct {
     double* out;
     const int64_t* rows; /* flat indices into [B, Lq, Hq]; NULL = all rows in order */
     int64_t nrows;
-    int B, Hq, Hkv, Lq, Lk, d, causal;
+    int B, Hq, Hkv, Lq, Lk, d;
+    int64_t win_left, win_right; /* visible keys of query i: [i+s-win_left, i+s+win_right], s = Lk-Lq; <0 = unbounded */
     double scale;
     int tid, nthreads;
 } attn_job;
 
 /* One query row: s_j = scale * <q_i, k_j> for every visible key j, then
- * o = sum_j softmax(s)_j v_j. Causal visibility: key j is visible to query i when
- * j <= i + (Lk - Lq) (the query block sits at the end of the key sequence). */
+ * o = sum_j softmax(s)_j v_j. The query block sits at the end of the key sequence: query i is
+ * at key position i + (Lk - Lq). Visible keys: j >= i + (Lk - Lq) - win_left (if win_left >= 0)
+ * and j <= i + (Lk - Lq) + win_right (if win_right >= 0). Causal is (win_left, win_right) = (-1, 0). */
 static void attention_row(const attn_job* J, int64_t row, double* scores, double* o) {
     int64_t h = row % J->Hq;
     int64_t i = (row / J->Hq) % J->Lq;
@@ -121,29 +123,29 @@ static void attention_row(const attn_job* J, int64_t row, double* scores, double
     int64_t hk = h / group;
     int d = J->d;
     const double* qi = J->q + row * d;
-    int64_t nvis = J->Lk;
-    if (J->causal) {
-        int64_t last = i + (J->Lk - J->Lq);
-        nvis = last + 1 < J->Lk ? last + 1 : J->Lk;
-        if (nvis < 0) nvis = 0;
-    }
+    int64_t pos = i + (J->Lk - J->Lq);
+    int64_t jlo = 0, jhi = J->Lk - 1;
+    if (J->win_left >= 0 && pos - J->win_left > jlo) jlo = pos - J->win_left;
+    if (J->win_right >= 0 && pos + J->win_right < jhi) jhi = pos + J->win_right;
+    int64_t nvis = jhi >= jlo ? jhi - jlo + 1 : 0;
     double m = -INFINITY;
-    for (int64_t j = 0; j < nvis; ++j) {
+    for (int64_t n = 0; n < nvis; ++n) {
+        int64_t j = jlo + n;
         const double* kj = J->k + (((int64_t)b * J->Lk + j) * J->Hkv + hk) * d;
         double dot = 0.0;
         for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
-        scores[j] = J->scale * dot;
-        if (scores[j] > m) m = scores[j];
+        scores[n] = J->scale * dot;
+        if (scores[n] > m) m = scores[n];
     }
     double l = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) {
-        scores[j] = exp(scores[j] - m);
-        l += scores[j];
+    for (int64_t n = 0; n < nvis; ++n) {
+        scores[n] = exp(scores[n] - m);
+        l += scores[n];
     }
     for (int t = 0; t < d; ++t) o[t] = 0.0;
-    for (int64_t j = 0; j < nvis; ++j) {
-        const double* vj = J->v + (((int64_t)b * J->Lk + j) * J->Hkv + hk) * d;
-        for (int t = 0; t < d; ++t) o[t] += scores[j] * vj[t];
+    for (int64_t n = 0; n < nvis; ++n) {
+        const double* vj = J->v + (((int64_t)b * J->Lk + jlo + n) * J->Hkv + hk) * d;
+        for (int t = 0; t < d; ++t) o[t] += scores[n] * vj[t];
     }
     for (int t = 0; t < d; ++t) o[t] = o[t] / l;
 }
@@ -161,12 +163,13 @@ static void* attention_worker(void* arg) {
 }
 
 /* q: [B, Lq, Hq, d], k and v: [B, Lk, Hkv, d], contiguous fp64. Query head h reads key/value
- * head h / (Hq / Hkv). out: [nrows, d], row n is the attention output of query row rows[n]
+ * head h / (Hq / Hkv). Visible keys per query as in attention_row (win_left = win_right = -1:
+ * all keys; (-1, 0): causal). out: [nrows, d], row n is the attention output of query row rows[n]
  * (flat index (b * Lq + i) * Hq + h), or of row n when rows is NULL (then nrows = B*Lq*Hq).
  * Returns 0 on success, -1 on invalid arguments or allocation failure. */
 int oracle_attention(const double* q, const double* k, const double* v, double* out,
                      const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
-                     double scale, int causal, int nthreads) {
+                     double scale, int64_t win_left, int64_t win_right, int nthreads) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq < 0 || Lk < 0 || d <= 0) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -175,7 +178,7 @@ int oracle_attention(const double* q, const double* k, const double* v, double* 
     int created[256];
     int rc = 0;
     for (int t = 0; t < nthreads; ++t) {
-        attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, causal, scale, t, nthreads};
+        attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, win_left, win_right, scale, t, nthreads};
         jobs[t] = J;
         created[t] = 0;
     }

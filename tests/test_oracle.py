@@ -315,3 +315,51 @@ def test_qk_norm_rope_order_is_norm_then_rope():
     # with gamma = 1 the rotation preserves the unit RMS of each head
     out1 = oracle.qk_norm_rope(z, np.ones(d), 0.0, ang, oracle.SPLIT)
     np.testing.assert_allclose(np.sqrt((out1 ** 2).mean(axis=-1)), 1.0, rtol=1e-13)
+
+
+# ------------------------------------------------------------------ local window (left, right)
+
+def _band_mask(Lq, Lk, left, right):
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    m = np.ones((Lq, Lk), dtype=bool)
+    if left >= 0:
+        m &= j >= pos - left
+    if right >= 0:
+        m &= j <= pos + right
+    return torch.from_numpy(m)
+
+
+@pytest.mark.parametrize("Lq,Lk,left,right", [(9, 9, 2, 1), (5, 12, 3, 0), (7, 20, -1, 2), (11, 11, 4, -1)])
+def test_window_matches_banded_sdpa(Lq, Lk, left, right):
+    q, k, v = _rand(2, Lq, 2, 8), _rand(2, Lk, 2, 8), _rand(2, Lk, 2, 8)
+    out = oracle.attention(q, k, v, 0.4, window=(left, right))
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.4, mask=_band_mask(Lq, Lk, left, right)),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_window_special_cases():
+    q, k, v = _rand(1, 6, 2, 8), _rand(1, 10, 2, 8), _rand(1, 10, 2, 8)
+    full = oracle.attention(q, k, v, 0.3)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, 0.3, window=(-1, -1)), full)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, 0.3, window=(10, 10)), full)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, 0.3, window=(-1, 0)),
+                                  oracle.attention(q, k, v, 0.3, causal=True))
+    # (0, 0): query i sees only key i + Lk - Lq
+    diag = oracle.attention(q, k, v, 0.3, window=(0, 0))
+    np.testing.assert_allclose(diag, v[:, 4:10], rtol=0, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, 0.3, causal=True, window=(1, 0))
+
+
+def test_window_two_keys_sigmoid():
+    # window (1, 0) on a square problem: row i >= 1 sees keys i-1 and i
+    q, k, v = _rand(1, 5, 1, 4), _rand(1, 5, 1, 4), _rand(1, 5, 1, 4)
+    out = oracle.attention(q, k, v, 0.8, window=(1, 0))
+    for i in range(1, 5):
+        s_prev = 0.8 * float(np.dot(q[0, i, 0], k[0, i - 1, 0]))
+        s_cur = 0.8 * float(np.dot(q[0, i, 0], k[0, i, 0]))
+        w_cur = 1.0 / (1.0 + math.exp(s_prev - s_cur))
+        np.testing.assert_allclose(out[0, i, 0], w_cur * v[0, i, 0] + (1.0 - w_cur) * v[0, i - 1, 0],
+                                   rtol=0, atol=1e-13)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 0], rtol=0, atol=1e-14)
