@@ -84,6 +84,12 @@ def make_workload(name: str, dev: str):
         q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
         out = torch.empty_like(q)
+        if w.attn_window is not None:
+            info["window"] = list(w.attn_window)
+
+            def step():
+                binding.attn_forward_window(q, k, v, out, w.scale, w.attn_window)
+            return w, step, step, info, (q, k, v)
         fwd = binding.attn_forward if w.dtype == "bf16" else binding.attn_forward_f16
 
         def step():
@@ -160,6 +166,31 @@ def make_workload(name: str, dev: str):
     return w, step, kern, info, None
 
 
+def visible_keys(w, i):
+    """Keys each query row i (array of query indices) attends to under the workload's mask."""
+    import numpy as np
+    p = i + (w.Lk - w.Lq)
+    lo, hi = np.zeros_like(p), np.full_like(p, w.Lk - 1)
+    if w.causal:
+        hi = np.minimum(hi, p)
+    if w.attn_window is not None:
+        left, right = w.attn_window
+        if left >= 0:
+            lo = np.maximum(lo, p - left)
+        if right >= 0:
+            hi = np.minimum(hi, p + right)
+    return hi - lo + 1
+
+
+def workload_flops(w) -> float:
+    """Flops per step: the metric's formula 4*B*H*Lq*Lk*d; a local-attention band counts only
+    the keys inside it (4*B*H*d*sum of visible keys), which is the work the band leaves."""
+    if w.attn_window is None:
+        return w.flops
+    import numpy as np
+    return 4.0 * w.B * w.Hq * w.d * float(visible_keys(w, np.arange(w.Lq)).sum())
+
+
 def time_loop(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -199,7 +230,7 @@ def cpu_baseline(w, tensors, target_s: float):
     def run(n):
         rows = np.sort(rng.choice(total, size=min(n, total), replace=False))
         t0 = time.perf_counter()
-        oracle.attention(qn, kn, vn, w.scale, w.causal, rows=rows, nthreads=threads)
+        oracle.attention(qn, kn, vn, w.scale, w.causal, rows=rows, nthreads=threads, window=w.attn_window)
         return rows, time.perf_counter() - t0
 
     n = max(threads * 4, 64)
@@ -210,13 +241,8 @@ def cpu_baseline(w, tensors, target_s: float):
     n_full = min(total, int(len(rows) * target_s / max(t, 1e-6)))
     if n_full > len(rows):
         rows, t = run(n_full)
-    # flops of the sampled rows by the metric's formula (causal rows: their visible keys)
-    if w.causal:
-        i = (rows // w.Hq) % w.Lq
-        keys = np.minimum(w.Lk, i + (w.Lk - w.Lq) + 1).sum()
-        fl = 4.0 * w.d * float(keys)
-    else:
-        fl = 4.0 * w.d * w.Lk * len(rows)
+    # flops of the sampled rows: 4*d per visible key of each row
+    fl = 4.0 * w.d * float(visible_keys(w, (rows // w.Hq) % w.Lq).sum())
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {total} query rows (random, seed 0), each over all its keys; "
                       f"{t:.1f} s wall, fp64, {threads} threads",
@@ -251,7 +277,7 @@ def main():
     if hbm:
         info["hbm_kernels"] = hbm
 
-    flops = w.flops
+    flops = workload_flops(w)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kern * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)

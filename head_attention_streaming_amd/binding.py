@@ -19,7 +19,7 @@ SA_NORM_NONE, SA_NORM_HEAD = 0, 1
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED = 0, 1, 2
 
 EXPORTS = ("qk_norm_rope", "kv_cache_slot", "kv_cache_append", "attn_forward", "attn_forward_f16",
-           "attn_forward_kvstride", "sa_last_error")
+           "attn_forward_kvstride", "attn_forward_window", "sa_last_error")
 
 _lib = None
 
@@ -49,6 +49,7 @@ def lib():
         L.attn_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
         L.attn_forward_f16.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
         L.attn_forward_kvstride.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I64, I, P]
+        L.attn_forward_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
         L.sa_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = I
@@ -104,6 +105,21 @@ def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = Fa
     _check("attn_forward_kvstride",
            lib().attn_forward_kvstride(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, int(Lk), d,
                                        float(scale), int(bool(causal)), kv_bstride, _dtype_code(q), _stream(q)))
+    return out
+
+
+def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk: int | None = None):
+    """Local attention: query i (key position p = i + Lk - Lq) sees keys [p - left, p + right].
+
+    window = (left, right), -1 for an unbounded side; k, v [B, S, Hkv, d] with S >= Lk
+    (Lk defaults to S). bf16 or fp16 for all four tensors.
+    """
+    B, Lq, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    left, right = (int(w) for w in window)
+    _check("attn_forward_window",
+           lib().attn_forward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
+                                     d, float(scale), left, right, S * Hkv * d, _dtype_code(q), _stream(q)))
     return out
 
 

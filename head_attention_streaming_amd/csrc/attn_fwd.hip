@@ -46,7 +46,8 @@ struct KParams {
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* out;
-    int Hq, Hkv, Lq, Lk, group, n_qblk, causal, nblocks;
+    int Hq, Hkv, Lq, Lk, group, n_qblk, nblocks;
+    int win_left, win_right;  // visible keys of query i: [i+s-left, i+s+right], s = Lk-Lq; -1 = unbounded
     int64_t q_bstride, kv_bstride;
     int q_tstride, kv_tstride;
     float c;  // scale * log2(e)
@@ -148,20 +149,35 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     const int bh = bid / p.n_qblk;
     const int h = bh % p.Hq;
     const int b = bh / p.Hq;
-    if (p.causal) qblk = p.n_qblk - 1 - qblk;  // longest rows first
+    if (p.win_right >= 0) qblk = p.n_qblk - 1 - qblk;  // causal-like bands: longest rows first
     const int hk = h / p.group;
 
     const int qb0 = qblk * kBM;
     const int r0 = qb0 + wave * 32;  // this wave's first query row
     const int qrow = r0 + j;
-    const int shift = p.Lk - p.Lq;   // causal: query i sees keys j <= i + shift
+    const int shift = p.Lk - p.Lq;   // query i sits at key position i + shift
+    const int qlast = min(qb0 + kBM, p.Lq) - 1;
 
-    int kend = p.Lk;
-    if (p.causal) kend = min(p.Lk, min(qb0 + kBM, p.Lq) - 1 + shift + 1);
+    // Key tiles [t0, nkt) hold every key some row of the workgroup can see. Tiles in [t0, tl)
+    // cut the left window edge and tiles in [tr, nkt) the right edge or the key tail for some
+    // row; only those get per-element masks.
+    const int kbeg = p.win_left >= 0 ? max(0, qb0 + shift - p.win_left) : 0;
+    const int kend = p.win_right >= 0 ? min(p.Lk, qlast + shift + p.win_right + 1) : p.Lk;
+    const int t0 = kbeg / kBN;
     const int nkt = (kend + kBN - 1) / kBN;
-    // first tile that needs a mask for some row of the workgroup (tail keys or causal diagonal)
-    int t_mask = p.Lk / kBN;
-    if (p.causal) t_mask = min(t_mask, max(0, (qb0 + shift + 1) / kBN));
+    int tl = t0;
+    if (p.win_left >= 0) tl = max(t0, (qlast + shift - p.win_left + kBN - 1) / kBN);
+    int tr = p.Lk / kBN;
+    if (p.win_right >= 0) tr = min(tr, max(0, (qb0 + shift + p.win_right + 1) / kBN));
+    // this lane's visible keys [key_lo, key_lo + key_span] (rows past Lq may get an empty or
+    // wrapped range; their scores are never stored)
+    int key_lo, key_hi;
+    {
+        const int64_t pos = (int64_t)qrow + shift;
+        key_lo = p.win_left >= 0 ? (int)max<int64_t>(0, pos - p.win_left) : 0;
+        key_hi = p.win_right >= 0 ? (int)min<int64_t>(p.Lk - 1, pos + p.win_right) : p.Lk - 1;
+    }
+    const unsigned key_span = (unsigned)(key_hi - key_lo);
 
     // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row.
     u32x4 qf[DC];
@@ -286,15 +302,15 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 }
         }
         if constexpr (QK) {
-            const int k0 = t * kBN;
             if constexpr (MASK) {
+                // one unsigned compare and a select per score: key - key_lo in [0, key_span]
+                const int rel0 = t * kBN + 4 * g - key_lo;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const bool ok = key < p.Lk && (!p.causal || key <= qrow + shift);
-                        if (!ok) sc[kb][r] = -INFINITY;
+                        const unsigned rel = (unsigned)(rel0 + kb * 32 + 8 * (r >> 2) + (r & 3));
+                        sc[kb][r] = rel <= key_span ? sc[kb][r] : -INFINITY;
                     }
             }
             float mk[KB];
@@ -323,9 +339,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // steps 1 .. nkt-1 with both halves; S(t) in s0 for even t, s1 for odd t
-    auto middle = [&](auto do_mask, int t0, int t1) __attribute__((always_inline)) {
-        int t = t0;
+    // steps t in [a, b) with both halves; S(t) lives in s0 for even t, s1 for odd t
+    auto middle = [&](auto do_mask, int ta, int t1) __attribute__((always_inline)) {
+        int t = ta;
         if (t < t1 && (t & 1)) step(T_{}, T_{}, do_mask, t++, s1, s0);
         for (; t + 1 < t1; t += 2) {
             step(T_{}, T_{}, do_mask, t, s0, s1);
@@ -334,17 +350,26 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         if (t < t1) step(T_{}, T_{}, do_mask, t, s0, s1);
     };
 
-    if (nkt > 0) {
-        load_k(0);
-        store_k(0);
-        load_k(min(1, nkt - 1));
-        load_v(0);
+    if (nkt > t0) {
+        load_k(t0);
+        store_k(t0 & 1);
+        load_k(min(t0 + 1, nkt - 1));
+        load_v(t0);
         __syncthreads();
-        if (t_mask == 0) step(T_{}, F_{}, T_{}, 0, s0, s1);
-        else step(T_{}, F_{}, F_{}, 0, s0, s1);
-        const int tm = max(1, min(t_mask, nkt));
-        middle(F_{}, 1, tm);
-        middle(T_{}, tm, nkt);
+        const bool mask0 = t0 < tl || t0 >= tr;
+        if (t0 & 1) {
+            if (mask0) step(T_{}, F_{}, T_{}, t0, s1, s0);
+            else step(T_{}, F_{}, F_{}, t0, s1, s0);
+        } else {
+            if (mask0) step(T_{}, F_{}, T_{}, t0, s0, s1);
+            else step(T_{}, F_{}, F_{}, t0, s0, s1);
+        }
+        // steps t0+1 .. nkt-1 in three segments: left-edge masked, unmasked, right-edge masked
+        const int e1 = min(max(tl, t0 + 1), nkt);
+        const int e2 = max(e1, min(tr, nkt));
+        middle(T_{}, t0 + 1, e1);
+        middle(F_{}, e1, e2);
+        middle(T_{}, e2, nkt);
         if (nkt & 1) step(F_{}, T_{}, F_{}, nkt, s1, s0);  // S(nkt-1) in s0 when nkt-1 is even
         else step(F_{}, T_{}, F_{}, nkt, s0, s1);
     }
@@ -402,7 +427,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     p.Lk = a.Lk;
     p.group = a.Hq / a.Hkv;
     p.n_qblk = (a.Lq + kBM - 1) / kBM;
-    p.causal = a.causal;
+    p.win_left = a.win_left;
+    p.win_right = a.win_right;
     p.q_bstride = a.q_bstride;
     p.kv_bstride = a.kv_bstride;
     p.q_tstride = a.Hq * D;

@@ -44,7 +44,7 @@ int64_t mul4(int64_t a, int64_t b, int64_t c, int64_t d) {
 }
 
 int check_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
-               int Lk, int d, float scale, int causal, int64_t kv_bstride, int dtype) {
+               int Lk, int d, float scale, int win_left, int win_right, int64_t kv_bstride, int dtype) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lq < 0 || Lk < 0)
         return fail(SA_ERR_RANGE, "attn_forward: negative or zero size (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d)", B, Hq,
                     Hkv, Lq, Lk);
@@ -52,8 +52,13 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
         return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0) or f16 (1)", dtype);
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward: head dim %d not built (64, 128)", d);
     if (Hq % Hkv != 0) return fail(SA_ERR_SHAPE, "attn_forward: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-    if (causal != 0 && causal != 1) return fail(SA_ERR_RANGE, "attn_forward: causal must be 0 or 1");
-    if (causal && Lq > Lk) return fail(SA_ERR_SHAPE, "attn_forward: causal needs Lq <= Lk (Lq=%d Lk=%d)", Lq, Lk);
+    if (win_left < -1 || win_right < -1)
+        return fail(SA_ERR_RANGE, "attn_forward: window bounds must be >= -1 (left=%d right=%d)", win_left, win_right);
+    // with a right bound every query must see at least one key: the first query's band ends at
+    // Lk - Lq + win_right, which must not fall before key 0
+    if (win_right >= 0 && (int64_t)Lq > (int64_t)Lk + win_right)
+        return fail(SA_ERR_SHAPE, "attn_forward: causal or right-bounded window needs Lq <= Lk + right (Lq=%d Lk=%d right=%d)",
+                    Lq, Lk, win_right);
     if (!(scale > 0.f) || scale > 1e30f) return fail(SA_ERR_RANGE, "attn_forward: scale must be positive and finite");
     if (B == 0 || Lq == 0) return SA_OK + 1;  // nothing to do
     if (Lk == 0) return fail(SA_ERR_SHAPE, "attn_forward: Lk must be >= 1 when Lq > 0");
@@ -74,8 +79,8 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
 }
 
 int run_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk, int d,
-             float scale, int causal, int64_t kv_bstride, int dtype, void* stream) {
-    const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, kv_bstride, dtype);
+             float scale, int win_left, int win_right, int64_t kv_bstride, int dtype, void* stream) {
+    const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, kv_bstride, dtype);
     if (st < 0) return st;
     if (st > 0) return ok();
     sa::AttnArgs a;
@@ -92,9 +97,16 @@ int run_attn(const void* q, const void* k, const void* v, void* out, int B, int 
     a.q_bstride = (int64_t)Lq * Hq * d;
     a.kv_bstride = kv_bstride;
     a.scale = scale;
-    a.causal = causal;
+    // A bound that every query's band already reaches is dropped: query i sits at key i + Lk - Lq,
+    // so left >= Lk - 1 reaches key 0 for all queries and right >= Lq - 1 reaches key Lk - 1.
+    a.win_left = win_left >= Lk - 1 ? -1 : win_left;
+    a.win_right = win_right >= Lq - 1 ? -1 : win_right;
     a.dtype = dtype;
     return hip_status(sa::launch_attn_fwd(a, static_cast<hipStream_t>(stream)), "attn_forward launch");
+}
+
+int check_causal(int causal) {
+    return causal == 0 || causal == 1 ? SA_OK : fail(SA_ERR_RANGE, "attn_forward: causal must be 0 or 1");
 }
 
 }  // namespace
@@ -105,19 +117,29 @@ const char* sa_last_error(void) { return g_err; }
 
 int attn_forward(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk,
                  int d, float scale, int causal, void* stream) {
-    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, (int64_t)Lk * Hkv * d, SA_DTYPE_BF16,
-                    stream);
+    if (check_causal(causal)) return SA_ERR_RANGE;
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, -1, causal ? 0 : -1, (int64_t)Lk * Hkv * d,
+                    SA_DTYPE_BF16, stream);
 }
 
 int attn_forward_f16(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
                      int Lk, int d, float scale, int causal, void* stream) {
-    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, (int64_t)Lk * Hkv * d, SA_DTYPE_F16,
-                    stream);
+    if (check_causal(causal)) return SA_ERR_RANGE;
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, -1, causal ? 0 : -1, (int64_t)Lk * Hkv * d,
+                    SA_DTYPE_F16, stream);
 }
 
 int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
                           int Lk, int d, float scale, int causal, int64_t kv_bstride, int dtype, void* stream) {
-    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, causal, kv_bstride, dtype, stream);
+    if (check_causal(causal)) return SA_ERR_RANGE;
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, -1, causal ? 0 : -1, kv_bstride, dtype, stream);
+}
+
+int attn_forward_window(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
+                        int Lk, int d, float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                        void* stream) {
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype,
+                    stream);
 }
 
 int kv_cache_slot(int64_t chunk_idx, int chunk_len, int sink_size, int window_size, int64_t* slot_base_out,

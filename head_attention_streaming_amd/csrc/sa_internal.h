@@ -15,7 +15,8 @@ struct AttnArgs {
     int64_t q_bstride;   // between batches of q and out (= Lq*Hq*d)
     int64_t kv_bstride;  // between batches of k and v
     float scale;
-    int causal;
+    int win_left;        // visible keys of query i: [i+s-win_left, i+s+win_right], s = Lk - Lq;
+    int win_right;       // -1 = unbounded (causal is (-1, 0))
     int dtype;           // SA_DTYPE_*
 };
 

@@ -78,6 +78,7 @@ class Workload:
     prologue: str = "none"   # "none" | "qk_norm_rope" (streaming self-attention) | "q_norm" (cross)
     chunk: int = 0           # streaming: chunk length (= Lq)
     window: int = 0          # streaming: cache capacity in tokens (sink 0)
+    attn_window: tuple | None = None  # local attention band (left, right) around i + Lk - Lq
 
     @property
     def flops(self) -> float:
@@ -99,4 +100,7 @@ WORKLOADS = {
     # long non-causal MHA, [1, 20480, 56, 128] bf16
     "mha_20480_bf16": Workload("mha_20480_bf16", 1, 56, 56, 20480, 20480, 128, "bf16", False,
                                128 ** -0.5, 1005),
+    # sliding-window (local) attention, [4, 4096, 32, 64] fp16, 256 keys back + the query's own
+    "window_4096_w256_f16": Workload("window_4096_w256_f16", 4, 32, 32, 4096, 4096, 64, "f16", False,
+                                     0.125, 1006, attn_window=(256, 0)),
 }

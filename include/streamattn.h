@@ -156,6 +156,25 @@ int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out
                           int B, int Hq, int Hkv, int Lq, int Lk, int d,
                           float scale, int causal, int64_t kv_bstride, int dtype, void* stream);
 
+/*
+ * attn_forward_window -- local (sliding-window) attention over a K/V buffer with batch stride.
+ *
+ * Page "optimizing-attention-flash", workflow 2, "Step 3: Enable advanced features": sliding
+ * window (local) attention, a (left, right) window around each query. Query i sits at key
+ * position p_i = i + (Lk - Lq) (queries aligned to the end of the keys, as with causal) and
+ * sees key j iff p_i - window_left <= j <= p_i + window_right; a bound of -1 is unbounded.
+ * (-1, 0) is causal attention, (-1, -1) full attention; a causal window of w tokens back is
+ * (w, 0), the page's causal=True with a left window.
+ *   window_left, window_right  >= -1. With window_right >= 0, Lq <= Lk + window_right is
+ *            required so that every query sees at least one key (SA_ERR_SHAPE otherwise).
+ * Key tiles that lie outside every query's band of a workgroup are skipped, so the work is
+ * proportional to the keys in the band. Everything else as attn_forward_kvstride.
+ */
+int attn_forward_window(const void* q, const void* k, const void* v, void* out,
+                        int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                        float scale, int window_left, int window_right,
+                        int64_t kv_bstride, int dtype, void* stream);
+
 /* Text describing the last non-zero status returned to this thread ("" if none). */
 const char* sa_last_error(void);
 

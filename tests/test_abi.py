@@ -115,3 +115,24 @@ def test_kv_cache_slot_large_chunk_index():
     assert vis == 96 and slot == 32 + ((10 ** 15 - 2) % 4) * 16
     with pytest.raises(binding.StreamAttnError):
         binding.kv_cache_slot(-1, 16, 0, 64)
+
+
+def _win(left, right, Lq=16, Lk=16, q=1):
+    P = lambda x: None if x is None else ctypes.c_void_p(x * 4096)
+    return lib().attn_forward_window(P(q), P(1), P(1), P(16), 1, 8, 8, Lq, Lk, 128, 0.1, left, right,
+                                     Lk * 8 * 128, 0, None)
+
+
+@pytest.mark.parametrize("left,right,Lq,Lk,code", [
+    (-2, 0, 16, 16, -5), (4, -7, 16, 16, -5),          # bounds below -1
+    (4, 0, 20, 16, -2),                                # causal band with Lq > Lk: first query sees nothing
+    (-1, 3, 20, 16, -2),                               # Lq > Lk + right
+])
+def test_attn_forward_window_rejects_bad_arguments(left, right, Lq, Lk, code):
+    assert _win(left, right, Lq, Lk) == code
+    assert lib().sa_last_error().decode() != ""
+
+
+def test_attn_forward_window_accepts_lq_up_to_lk_plus_right():
+    # Lq = Lk + right passes shape validation; the null q pointer is what stops the call
+    assert _win(-1, 4, 20, 16, q=None) == -1
