@@ -116,7 +116,8 @@ def make_workload(name: str, dev: str):
 
     # streaming self-attention: steady state (cache full, every step evicts the oldest chunk)
     Lc, S = w.chunk, w.window
-    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, device=dev)
+    after = w.rope_scope == "after"
+    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, device=dev, after_cache_rope=after)
     g = torch.Generator().manual_seed(w.seed)
     gq, gk = synthetic.norm_weight(w.d, g).to(dev), synthetic.norm_weight(w.d, g).to(dev)
     nsets = 6  # rotate input sets (6 x 55 MB) so the prologue and append are not served from cache
@@ -127,29 +128,39 @@ def make_workload(name: str, dev: str):
     q_buf = torch.empty((w.B, Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(q_buf)
     state = {"c": 0}
-    angles = [synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), w.d).to(dev) for c in range(8)]
+    if after:  # rows 0 .. visible-1 of the visible sequence (visible = S once the cache is full)
+        vis_angles = synthetic.rope_angles(np.arange(S), w.d).to(dev)
+        angles = [vis_angles[:min(S, (c + 1) * Lc)] for c in range(8)]
+    else:      # absolute stream positions of chunk c
+        angles = [synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), w.d).to(dev) for c in range(8)]
 
     def step():
         c = state["c"]
         q, k, v = sets[c % nsets]
-        binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[c % 8], 1e-6, w.scale)
+        binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[min(c, 7)], 1e-6, w.scale)
         state["c"] = c + 1
 
     for _ in range(S // Lc):  # fill the cache before timing
         step()
 
     def kern():
-        binding.attn_forward_kvstride(q_buf, cache.k, cache.v, out, S, w.scale, False)
+        binding.attn_forward_kvstride(q_buf, cache.k_rot if after else cache.k, cache.v, out, S, w.scale, False)
 
     # the HBM-bound steps alone, on rotating input sets (each set is read once per 6 calls)
     rot = {"i": 0}
     slot = cache.slot_base
 
-    def prologue():
+    q_ang = angles[7][S - Lc:] if after else angles[0]
+    flag = binding.SA_ROPE_AFTER_CACHE if after else 0
+    gq_in = synthetic.norm_weight(w.Hq * w.d, g).to(dev)
+    gk_in = synthetic.norm_weight(w.Hkv * w.d, g).to(dev)
+
+    def prologue(scope=binding.SA_NORM_HEAD):
         q, k, _ = sets[rot["i"] % nsets]
         rot["i"] += 1
-        binding.qk_norm_rope(q, q_buf, k, cache.k[:, slot:], gq, gk, angles[0], 1e-6, binding.SA_NORM_HEAD,
-                             binding.SA_ROPE_SPLIT, k_out_bstride=S * w.Hkv * w.d)
+        inner = scope == binding.SA_NORM_INNER
+        binding.qk_norm_rope(q, q_buf, k, cache.k[:, slot:], gq_in if inner else gq, gk_in if inner else gk, q_ang,
+                             1e-6, scope, binding.SA_ROPE_SPLIT | flag, k_out_bstride=S * w.Hkv * w.d)
 
     def append():
         _, _, v = sets[rot["i"] % nsets]
@@ -159,9 +170,19 @@ def make_workload(name: str, dev: str):
     elem = 2 * w.B * Lc * w.Hq * w.d  # bytes of one [B, Lc, H, d] bf16 tensor
     info["hbm_steps"] = {
         "qk_norm_rope": (prologue, 4 * elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4),  # q,k read + written, angles, gammas
+        "qk_norm_rope_inner": (lambda: prologue(binding.SA_NORM_INNER),
+                               4 * elem + Lc * (w.d // 2) * 4 + 2 * w.Hq * w.d * 4),  # inner-scope weights
         "kv_cache_append": (append, 2 * elem),                                   # v read + written
     }
-    info["step"] = "qk_norm_rope(Q,K->cache) + kv_cache_append(V) + attn_forward_kvstride, cache full"
+    if after:
+        def cache_rope():
+            binding.kv_cache_rope(cache.k, cache.k_rot, angles[7], state["c"] - 1, Lc, 0, S, binding.SA_ROPE_SPLIT)
+        kbytes = 2 * w.B * S * w.Hkv * w.d
+        info["hbm_steps"]["kv_cache_rope"] = (cache_rope, 2 * kbytes + S * (w.d // 2) * 4)  # cache K read, k_rot written, angles
+        info["step"] = ("qk_norm_rope(Q rotated, K normalised->cache) + kv_cache_append(V) + "
+                        "kv_cache_rope(visible K -> k_rot) + attn_forward_kvstride, cache full")
+    else:
+        info["step"] = "qk_norm_rope(Q,K->cache) + kv_cache_append(V) + attn_forward_kvstride, cache full"
     info["cache_tokens"] = S
     return w, step, kern, info, None
 

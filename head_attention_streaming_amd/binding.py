@@ -15,11 +15,11 @@ import torch
 from . import build as _build
 
 SA_DTYPE_BF16, SA_DTYPE_F16 = 0, 1
-SA_NORM_NONE, SA_NORM_HEAD = 0, 1
-SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED = 0, 1, 2
+SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
+SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
 
-EXPORTS = ("qk_norm_rope", "kv_cache_slot", "kv_cache_append", "attn_forward", "attn_forward_f16",
-           "attn_forward_kvstride", "attn_forward_window", "sa_last_error")
+EXPORTS = ("qk_norm_rope", "kv_cache_slot", "kv_cache_positions", "kv_cache_append", "kv_cache_rope",
+           "attn_forward", "attn_forward_f16", "attn_forward_kvstride", "attn_forward_window", "sa_last_error")
 
 _lib = None
 
@@ -46,6 +46,8 @@ def lib():
         L.qk_norm_rope.argtypes = [P, P, I64, P, P, I64, P, P, P, I, I, I, I, I, F, I, I, P]
         L.kv_cache_slot.argtypes = [I64, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I)]
         L.kv_cache_append.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, P]
+        L.kv_cache_positions.argtypes = [I64, I, I, I, ctypes.POINTER(I64), I]
+        L.kv_cache_rope.argtypes = [P, P, P, I, I, I, I, I, I, I64, I, P]
         L.attn_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
         L.attn_forward_f16.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
         L.attn_forward_kvstride.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I64, I, P]
@@ -126,9 +128,10 @@ def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk:
 def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None, angles=None, eps: float = 1e-6,
                  norm_scope: int = SA_NORM_HEAD, rope_style: int = SA_ROPE_SPLIT, q_out_bstride=None,
                  k_out_bstride=None, Hkv: int | None = None):
-    """Per-head RMSNorm then RoPE of q_in (and k_in) into q_out (and k_out), bf16.
+    """RMSNorm (head or inner scope) then RoPE of q_in (and k_in) into q_out (and k_out), bf16.
 
     q_in [B, L, Hq, d]; k_out may be a view of a cache row range (pass k_out_bstride = S*Hkv*d).
+    rope_style | SA_ROPE_AFTER_CACHE rotates the queries only (keys are normalised, unrotated).
     """
     B, L, Hq, d = q_in.shape
     if Hkv is None:
@@ -151,6 +154,25 @@ def kv_cache_slot(chunk_idx: int, chunk_len: int, sink_size: int, window_size: i
     return slot.value, vis.value
 
 
+def kv_cache_positions(chunk_idx: int, chunk_len: int, sink_size: int, window_size: int):
+    """Logical (arrival-order) row of each visible physical cache row after chunk ``chunk_idx``."""
+    _, vis = kv_cache_slot(chunk_idx, chunk_len, sink_size, window_size)
+    out = (ctypes.c_int64 * max(vis, 1))()
+    _check("kv_cache_positions", lib().kv_cache_positions(int(chunk_idx), int(chunk_len), int(sink_size),
+                                                          int(window_size), out, vis))
+    return [out[i] for i in range(vis)]
+
+
+def kv_cache_rope(cache_k, k_rot, angles, chunk_idx: int, chunk_len: int, sink_size: int, window_size: int,
+                  rope_style: int = SA_ROPE_SPLIT):
+    """After-cache RoPE: rotate the visible rows of cache_k [B, S, Hkv, d] into k_rot (same shape)
+    with angles [visible_len, d/2] indexed by logical row."""
+    B, S, Hkv, d = cache_k.shape
+    _check("kv_cache_rope", lib().kv_cache_rope(_ptr(cache_k), _ptr(k_rot), _ptr(angles), B, Hkv, d, int(chunk_len),
+                                                int(sink_size), int(window_size), int(chunk_idx), int(rope_style),
+                                                _stream(cache_k)))
+
+
 def kv_cache_append(k_new, v_new, cache_k, cache_v, chunk_idx: int, sink_size: int, window_size: int):
     """Copy k_new / v_new [B, Lc, Hkv, d] (either may be None) into their cache slot range."""
     ref = v_new if v_new is not None else k_new
@@ -167,12 +189,14 @@ class BlockKVCache:
     """
 
     def __init__(self, B: int, Hkv: int, d: int, chunk_len: int, sink_size: int, window_size: int,
-                 dtype=torch.bfloat16, device="cuda"):
+                 dtype=torch.bfloat16, device="cuda", after_cache_rope: bool = False):
         self.B, self.Hkv, self.d = B, Hkv, d
         self.chunk_len, self.sink_size, self.window_size = chunk_len, sink_size, window_size
         S = sink_size + window_size
         self.k = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
         self.v = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
+        # after-cache RoPE: the cache keeps unrotated keys; each step rotates the visible ones here
+        self.k_rot = torch.empty_like(self.k) if after_cache_rope else None
         self.slot_base = 0
         self.visible_len = 0
         self._current = None
@@ -201,18 +225,31 @@ class BlockKVCache:
 
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
-                               rope_style: int = SA_ROPE_SPLIT):
-    """One streaming self-attention chunk with before-cache RoPE, as four library calls:
+                               rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD):
+    """One streaming self-attention chunk as library calls between before_update / after_update.
 
-    before_update -> qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot) ->
-    kv_cache_append (v_in -> cache values) -> attn_forward_kvstride over the visible cache ->
-    after_update. Returns the visible length used.
+    Before-cache RoPE (cache.k_rot is None): angles [Lc, d/2] for the chunk's positions;
+    qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot, both rotated) ->
+    kv_cache_append (v_in -> cache values) -> attn_forward_kvstride over the visible cache.
+    After-cache RoPE (cache built with after_cache_rope=True): angles [visible_len, d/2] by
+    logical row; qk_norm_rope rotates q_in with the chunk's rows (the last Lc) and stores the
+    normalised keys unrotated -> kv_cache_append -> kv_cache_rope (visible keys -> cache.k_rot)
+    -> attn_forward_kvstride over cache.k_rot and the cached values.
+    Returns the visible length used.
     """
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
-    qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, angles, eps,
-                 SA_NORM_HEAD, rope_style, k_out_bstride=S * cache.Hkv * cache.d)
+    after = cache.k_rot is not None
+    q_angles = angles[visible - cache.chunk_len:visible] if after else angles
+    qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
+                 norm_scope, rope_style | (SA_ROPE_AFTER_CACHE if after else 0),
+                 k_out_bstride=S * cache.Hkv * cache.d)
     kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
-    attn_forward_kvstride(q_buf, cache.k, cache.v, out, visible, scale, False)
+    keys = cache.k
+    if after:
+        kv_cache_rope(cache.k, cache.k_rot, angles, chunk_idx, cache.chunk_len, cache.sink_size, cache.window_size,
+                      rope_style)
+        keys = cache.k_rot
+    attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
     cache.after_update(chunk_idx)
     return visible

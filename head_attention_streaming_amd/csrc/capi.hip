@@ -205,19 +205,23 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
     if (B < 0 || L < 0 || Hq <= 0 || (k_in && Hkv <= 0))
         return fail(SA_ERR_RANGE, "qk_norm_rope: negative or zero size");
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: head dim %d not built (64, 128)", d);
-    if (norm_scope != SA_NORM_NONE && norm_scope != SA_NORM_HEAD)
-        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: norm scope %d not built (none, head)", norm_scope);
-    if (rope_style < SA_ROPE_NONE || rope_style > SA_ROPE_INTERLEAVED)
+    if (norm_scope != SA_NORM_NONE && norm_scope != SA_NORM_HEAD && norm_scope != SA_NORM_INNER)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: unknown norm scope %d", norm_scope);
+    const int pairing = rope_style & ~SA_ROPE_AFTER_CACHE;
+    if ((rope_style & ~(SA_ROPE_AFTER_CACHE | 3)) || pairing > SA_ROPE_INTERLEAVED ||
+        (rope_style == SA_ROPE_AFTER_CACHE))
         return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: unknown RoPE style %d", rope_style);
+    if (norm_scope == SA_NORM_INNER && k_in && Hkv != Hq)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: inner-scope norm needs Hq == Hkv (grouped heads use head scope)");
     if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "qk_norm_rope: eps must be >= 0 and finite");
     if (B == 0 || L == 0) return ok();
     if (!q_in || !q_out) return fail(SA_ERR_NULL, "qk_norm_rope: null q pointer");
     if ((k_in == nullptr) != (k_out == nullptr)) return fail(SA_ERR_NULL, "qk_norm_rope: k_in and k_out must both be set or both NULL");
-    if (norm_scope == SA_NORM_HEAD && (!gamma_q || (k_in && !gamma_k)))
-        return fail(SA_ERR_NULL, "qk_norm_rope: RMSNorm weights required for head scope");
+    if (norm_scope != SA_NORM_NONE && (!gamma_q || (k_in && !gamma_k)))
+        return fail(SA_ERR_NULL, "qk_norm_rope: RMSNorm weights required");
     if (norm_scope == SA_NORM_NONE && (gamma_q || gamma_k))
         return fail(SA_ERR_SHAPE, "qk_norm_rope: weights given with norm scope none");
-    if ((rope_style != SA_ROPE_NONE) != (rope_angles != nullptr))
+    if ((pairing != SA_ROPE_NONE) != (rope_angles != nullptr))
         return fail(SA_ERR_NULL, "qk_norm_rope: angles must be given iff RoPE is enabled");
     for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out, (const void*)gamma_q,
                           (const void*)gamma_k})
@@ -228,8 +232,9 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
     if (k_in && (k_out_bstride < (int64_t)L * Hkv * d || k_out_bstride % 8))
         return fail(SA_ERR_SHAPE, "qk_norm_rope: bad k_out_bstride");
     if ((int64_t)B * L > INT32_MAX) return fail(SA_ERR_RANGE, "qk_norm_rope: grid too large");
-    sa::NormRopeArgs a;
+    sa::NormRopeArgs a{};
     a.q_in = q_in;
+    a.q_in_bstride = nq;
     a.q_out = q_out;
     a.q_out_bstride = q_out_bstride;
     a.k_in = k_in;
@@ -245,8 +250,62 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
     a.d = d;
     a.eps = eps;
     a.norm_scope = norm_scope;
-    a.rope_style = rope_style;
+    a.rope_style = pairing;
+    a.rope_keys = (rope_style & SA_ROPE_AFTER_CACHE) ? 0 : 1;
     return hip_status(sa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "qk_norm_rope launch");
+}
+
+int kv_cache_positions(int64_t chunk_idx, int chunk_len, int sink_size, int window_size, int64_t* logical_rows_out,
+                       int capacity) {
+    int64_t base = 0;
+    int vis = 0;
+    const int st = kv_cache_slot(chunk_idx, chunk_len, sink_size, window_size, &base, &vis);
+    if (st) return st;
+    if (!logical_rows_out) return fail(SA_ERR_NULL, "kv_cache_positions: null output pointer");
+    if (capacity < vis) return fail(SA_ERR_RANGE, "kv_cache_positions: output holds %d rows, %d visible", capacity, vis);
+    for (int s = 0; s < vis; ++s)
+        logical_rows_out[s] = sa::ring_logical_row(s, chunk_len, sink_size / chunk_len, window_size / chunk_len, chunk_idx);
+    return ok();
+}
+
+int kv_cache_rope(const void* cache_k, void* k_rot, const float* rope_angles, int B, int Hkv, int d, int chunk_len,
+                  int sink_size, int window_size, int64_t chunk_idx, int rope_style, void* stream) {
+    int64_t base = 0;
+    int vis = 0;
+    const int st = kv_cache_slot(chunk_idx, chunk_len, sink_size, window_size, &base, &vis);
+    if (st) return st;
+    if (B < 0 || Hkv <= 0) return fail(SA_ERR_RANGE, "kv_cache_rope: negative or zero size");
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "kv_cache_rope: head dim %d not built (64, 128)", d);
+    if (rope_style != SA_ROPE_SPLIT && rope_style != SA_ROPE_INTERLEAVED)
+        return fail(SA_ERR_UNSUPPORTED, "kv_cache_rope: RoPE style must be split or interleaved");
+    if (B == 0) return ok();
+    if (!cache_k || !k_rot || !rope_angles) return fail(SA_ERR_NULL, "kv_cache_rope: null pointer");
+    if (cache_k == k_rot) return fail(SA_ERR_SHAPE, "kv_cache_rope: k_rot must not be the cache (keys stay unrotated)");
+    if (!aligned16(cache_k) || !aligned16(k_rot))
+        return fail(SA_ERR_ALIGN, "kv_cache_rope: pointers must be 16-byte aligned");
+    const int64_t S = (int64_t)sink_size + window_size;
+    const int64_t bstride = mul4(S, Hkv, d, 1);
+    if (bstride < 0 || mul4(B, bstride, 1, 1) < 0 || (int64_t)B * vis > INT32_MAX)
+        return fail(SA_ERR_RANGE, "kv_cache_rope: cache too large");
+    sa::NormRopeArgs a{};
+    a.q_in = cache_k;
+    a.q_in_bstride = bstride;
+    a.q_out = k_rot;
+    a.q_out_bstride = bstride;
+    a.angles = rope_angles;
+    a.B = B;
+    a.L = vis;
+    a.Hq = Hkv;
+    a.Hkv = 0;
+    a.d = d;
+    a.norm_scope = SA_NORM_NONE;
+    a.rope_style = rope_style;
+    a.rope_keys = 1;
+    a.ring_lc = chunk_len;
+    a.ring_nsink = sink_size / chunk_len;
+    a.ring_nwin = window_size / chunk_len;
+    a.ring_chunk = chunk_idx;
+    return hip_status(sa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "kv_cache_rope launch");
 }
 
 }  // extern "C"

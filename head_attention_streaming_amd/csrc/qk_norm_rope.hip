@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     const int f0 = 8 * li;
 
     const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
-    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + ((int64_t)b * a.L + p) * a.Hq * D;
+    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + b * a.q_in_bstride + (int64_t)p * a.Hq * D;
     const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
     uint16_t* qout = static_cast<uint16_t*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
     uint16_t* kout = a.k_out ? static_cast<uint16_t*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
@@ -111,9 +111,10 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     load_batch(0);  // in flight while the angles are turned into cos/sin
 
     if (a.rope_style != 0) {
+        const int64_t arow = a.ring_lc > 0 ? ring_logical_row(p, a.ring_lc, a.ring_nsink, a.ring_nwin, a.ring_chunk) : p;
         for (int r = tid; r < HALF; r += kThreads) {
             float s, c;
-            sincosf(a.angles[(int64_t)p * HALF + r], &s, &c);
+            sincosf(a.angles[arow * HALF + r], &s, &c);
             cs[r] = c;
             sn[r] = s;
         }
@@ -136,10 +137,52 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
         }
     }
 
+    // Inner scope: one RMS over all of the token's query features (and one over its key
+    // features), so the sums of squares are reduced over the workgroup before any row is
+    // normalised. The first batch of rows is already in registers; later batches are read twice.
+    float r_q = 1.f, r_k = 1.f;
+    if (a.norm_scope == 2) {
+        float sq = 0.f, sk = 0.f;
+        for (int base = 0; base < rows_padded; base += NB * RPP) {
+            if (base > 0) load_batch(base);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = base + rs + nb * RPP;
+                float z[8];
+                unpack_bf16x8(raw[nb], z);  // zeros past the last row
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
+                if (row < a.Hq) sq += ss;
+                else sk += ss;
+            }
+        }
+        __shared__ float red[2][kThreads / 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            sq += __shfl_xor(sq, off);
+            sk += __shfl_xor(sk, off);
+        }
+        if ((tid & 63) == 0) {
+            red[0][tid >> 6] = sq;
+            red[1][tid >> 6] = sk;
+        }
+        __syncthreads();
+        sq = sk = 0.f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            sq += red[0][w];
+            sk += red[1][w];
+        }
+        r_q = 1.f / sqrtf(sq / (float)(a.Hq * D) + a.eps);
+        if (a.Hkv) r_k = 1.f / sqrtf(sk / (float)(a.Hkv * D) + a.eps);
+        if (rows_padded > NB * RPP) load_batch(0);
+    }
+
     float gq[8], gk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) gq[e] = gk[e] = 1.f;
-    if (a.norm_scope) {  // uniform: two 16-byte loads per weight vector
+    if (a.norm_scope == 1) {  // uniform: two 16-byte loads per weight vector
         const f32x4* pq = reinterpret_cast<const f32x4*>(a.gamma_q + f0);
         const f32x4 q0 = pq[0], q1 = pq[1];
 #pragma unroll
@@ -167,7 +210,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
             const bool is_q = row < a.Hq;
             float z[8];
             unpack_bf16x8(raw[nb], z);
-            if (a.norm_scope) {
+            if (a.norm_scope == 1) {
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
@@ -175,16 +218,28 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
                 const float r = 1.f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
+            } else if (a.norm_scope == 2 && valid) {
+                // weights of this row's features: gamma[h*d + f0 .. + 8]
+                const f32x4* pg = reinterpret_cast<const f32x4*>(
+                    is_q ? a.gamma_q + row * D + f0 : a.gamma_k + (row - a.Hq) * D + f0);
+                const f32x4 g0 = pg[0], g1 = pg[1];
+                const float r = is_q ? r_q : r_k;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[e] = g0[e] * (z[e] * r);
+                    z[e + 4] = g1[e] * (z[e + 4] * r);
+                }
             }
+            const int style = (is_q || a.rope_keys) ? a.rope_style : 0;  // uniform per row group
             float o[8];
-            if (a.rope_style == 1) {
+            if (style == 1) {
                 const bool first = li < LPR / 2;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float other = split_partner<LPR>(z[e]);
                     o[e] = first ? c8[e] * z[e] - s8[e] * other : s8[e] * other + c8[e] * z[e];
                 }
-            } else if (a.rope_style == 2) {
+            } else if (style == 2) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float x0 = z[2 * e], x1 = z[2 * e + 1];

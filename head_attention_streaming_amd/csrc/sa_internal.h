@@ -22,18 +22,36 @@ struct AttnArgs {
 
 struct NormRopeArgs {
     const void* q_in;
+    int64_t q_in_bstride;   // elements between batches of q_in (L*Hq*d when contiguous)
     void* q_out;
     int64_t q_out_bstride;
-    const void* k_in;
+    const void* k_in;       // [B, L, Hkv, d] contiguous, or null
     void* k_out;
     int64_t k_out_bstride;
-    const float* gamma_q;
-    const float* gamma_k;
-    const float* angles;
+    const float* gamma_q;   // [d] (head scope) or [Hq*d] (inner scope)
+    const float* gamma_k;   // [d] or [Hkv*d]
+    const float* angles;    // [rows, d/2]; row of token p: p, or its logical cache row (ring_lc > 0)
     int B, L, Hq, Hkv, d;
     float eps;
-    int norm_scope, rope_style;
+    int norm_scope;         // 0 none, 1 head, 2 inner
+    int rope_style;         // 0 none, 1 split, 2 interleaved
+    int rope_keys;          // rotate the k rows too (0: keys are normalised only)
+    int ring_lc, ring_nsink, ring_nwin;  // ring_lc > 0: token p is physical row p of a rolling
+    int64_t ring_chunk;                  // cache after chunk ring_chunk was written
 };
+
+// Rolling sink + window cache after chunk c has been written (sizes in chunks of Lc tokens):
+// the logical (arrival-order) row of physical row s, for s below the visible length. Sink
+// chunk u sits in slot u; window chunk c' sits in slot n_sink + (c' - n_sink) mod n_win; the
+// visible sequence is the sinks, then the window chunks oldest first.
+__host__ __device__ inline int64_t ring_logical_row(int64_t s, int Lc, int n_sink, int n_win, int64_t c) {
+    const int64_t u = s / Lc, i = s % Lc;
+    if (u < n_sink) return s;
+    const int64_t w = u - n_sink;                                   // window slot
+    const int64_t held = c - (((c - n_sink - w) % n_win) + n_win) % n_win;  // chunk in slot w
+    const int64_t first = c - n_win + 1 > n_sink ? c - n_win + 1 : n_sink;  // oldest visible window chunk
+    return ((int64_t)n_sink + (held - first)) * Lc + i;
+}
 
 struct CopyArgs {
     const void* src;

@@ -79,6 +79,7 @@ class Workload:
     chunk: int = 0           # streaming: chunk length (= Lq)
     window: int = 0          # streaming: cache capacity in tokens (sink 0)
     attn_window: tuple | None = None  # local attention band (left, right) around i + Lk - Lq
+    rope_scope: str = "before"        # streaming: RoPE before or after the K/V cache update
 
     @property
     def flops(self) -> float:
@@ -94,6 +95,9 @@ WORKLOADS = {
     # streaming self-attention: 40 heads, d 128, chunk 1785, rolling cache of 4 chunks (7140 keys)
     "stream_self_1785x4": Workload("stream_self_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
                                    128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140),
+    # the same streaming step with after-cache RoPE: unrotated cache, visible keys rotated per step
+    "stream_after_1785x4": Workload("stream_after_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
+                                    128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, rope_scope="after"),
     # cross-attention over a static 512-token context, B = 2 (guidance pair), Q RMSNorm only
     "cross_1785x512": Workload("cross_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
                                128 ** -0.5, 1004, "q_norm"),

@@ -46,20 +46,25 @@ typedef enum {
 
 enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1 };
 
-/* Q/K normalisation scope: none, or per head (m = d). Inner scope (m = Hq*d) is not built. */
-enum { SA_NORM_NONE = 0, SA_NORM_HEAD = 1 };
+/* Q/K normalisation scope: none, per head (m = d), or inner (m = H*d: all heads of a token). */
+enum { SA_NORM_NONE = 0, SA_NORM_HEAD = 1, SA_NORM_INNER = 2 };
 
-/* RoPE pairing: none, split-half pairs (r, r + d/2), interleaved pairs (2r, 2r + 1). */
-enum { SA_ROPE_NONE = 0, SA_ROPE_SPLIT = 1, SA_ROPE_INTERLEAVED = 2 };
+/* RoPE pairing: none, split-half pairs (r, r + d/2), interleaved pairs (2r, 2r + 1).
+ * SA_ROPE_AFTER_CACHE may be OR-ed into a pairing for qk_norm_rope: the queries are rotated,
+ * the keys only normalised (the cache stores unrotated keys; kv_cache_rope rotates them). */
+enum { SA_ROPE_NONE = 0, SA_ROPE_SPLIT = 1, SA_ROPE_INTERLEAVED = 2, SA_ROPE_AFTER_CACHE = 4 };
 
 /*
- * qk_norm_rope -- Q/K prologue: per-head RMSNorm, then RoPE, one rounding to bf16.
+ * qk_norm_rope -- Q/K prologue: RMSNorm, then RoPE, one rounding to bf16.
  *
  * Page "flashdreams.accelerated", section "Multi Head Attention Definition": the RMSNorm
- * equation gamma * z / sqrt(mean(z^2) + eps) with head scope (m = d, each head separately),
- * followed by the pair rotation [[cos t, -sin t], [sin t, cos t]] with angle t = theta_{p,r};
- * V is neither normalised nor rotated. With before-cache RoPE the rotated keys are what the
- * K/V cache stores, so k_out may point straight into a cache (see below).
+ * equation gamma * z / sqrt(mean(z^2) + eps) with head scope (m = d, each head separately) or
+ * inner scope (m = H*d, all heads of a token together), followed by the pair rotation
+ * [[cos t, -sin t], [sin t, cos t]] with angle t = theta_{p,r}; V is neither normalised nor
+ * rotated. With before-cache RoPE the rotated keys are what the K/V cache stores, so k_out may
+ * point straight into a cache (see below). With after-cache RoPE (rope_style |
+ * SA_ROPE_AFTER_CACHE) the keys are normalised and stored unrotated and only the queries are
+ * rotated here; kv_cache_rope rotates the visible keys before attention.
  *
  *   q_in      [B, L, Hq, d] bf16 (device). q_out: [B, L, Hq, d] bf16, batch stride
  *             q_out_bstride elements (>= L*Hq*d; q_out == q_in is allowed: in place).
@@ -68,8 +73,11 @@ enum { SA_ROPE_NONE = 0, SA_ROPE_SPLIT = 1, SA_ROPE_INTERLEAVED = 2 };
  *             k_out + b*k_out_bstride + (p*Hkv + h)*d. To write into a cache
  *             [B, S, Hkv, d] at token slot s0, pass cache_k + s0*Hkv*d and S*Hkv*d.
  *             NULL iff k_in is NULL.
- *   gamma_q, gamma_k  fp32 [d] RMSNorm weights; both NULL iff norm_scope == SA_NORM_NONE
- *             (gamma_k may be NULL when k_in is NULL).
+ *   gamma_q, gamma_k  fp32 RMSNorm weights, [d] for SA_NORM_HEAD, [Hq*d] / [Hkv*d] for
+ *             SA_NORM_INNER (16-byte aligned); both NULL iff norm_scope == SA_NORM_NONE
+ *             (gamma_k may be NULL when k_in is NULL). Inner scope with keys requires
+ *             Hq == Hkv (the accelerated-module guide rules out inner-width norms for grouped
+ *             heads); SA_ERR_UNSUPPORTED otherwise.
  *   rope_angles fp32 [L, d/2] host-built angles theta_{p,r} for the L positions of this chunk
  *             (device pointer); NULL iff rope_style == SA_ROPE_NONE. The same angles rotate q
  *             and k (positions are shared by the chunk's queries and keys).
@@ -120,6 +128,42 @@ int kv_cache_slot(int64_t chunk_idx, int chunk_len, int sink_size, int window_si
 int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* cache_v,
                     int B, int Lc, int Hkv, int d, int sink_size, int window_size,
                     int64_t chunk_idx, void* stream);
+
+/*
+ * kv_cache_positions -- logical row of every visible physical row of the rolling cache after
+ * chunk `chunk_idx` has been written. Pure host integer function (no device work).
+ *
+ * Same cache as kv_cache_slot. The visible keys in logical (arrival) order are the sink chunks,
+ * then the window chunks oldest first; physical row s holds logical row logical_rows_out[s] for
+ * s in [0, visible_len). This is the position order after-cache RoPE uses (kv_cache_rope).
+ *   logical_rows_out  HOST array of `capacity` >= visible_len entries.
+ * Returns SA_OK, SA_ERR_NULL, or SA_ERR_RANGE (as kv_cache_slot, or capacity too small).
+ */
+int kv_cache_positions(int64_t chunk_idx, int chunk_len, int sink_size, int window_size,
+                       int64_t* logical_rows_out, int capacity);
+
+/*
+ * kv_cache_rope -- after-cache RoPE: rotate every visible cached key for the current step.
+ *
+ * Page "flashdreams.accelerated", section "Multi Head Attention Definition", RoPE after the K/V
+ * cache update: the cache stores unrotated keys, and right before attention every visible key
+ * is rotated with the angles of its current position; the page "Accelerated building blocks"
+ * (section "Cache lifecycle") calls these cache-relative frequencies. The current position of
+ * a key is its logical row in the visible sequence (kv_cache_positions).
+ *   cache_k      [B, S, Hkv, d] bf16 unrotated keys, S = sink_size + window_size (device).
+ *   k_rot        [B, S, Hkv, d] bf16 output (device, must not be cache_k): rows
+ *                [0, visible_len) of every batch get the rotated keys of the same physical
+ *                rows, so attention over k_rot pairs each key with the value in its cache row.
+ *                Other rows are not written.
+ *   rope_angles  fp32 [visible_len, d/2] (device), row r = angles theta_{r, .} of logical row r;
+ *                the current chunk's queries use rows [visible_len - chunk_len, visible_len).
+ *   rope_style   SA_ROPE_SPLIT or SA_ROPE_INTERLEAVED.
+ * fp32 arithmetic, one rounding to bf16. Returns SA_OK or SA_ERR_* (kv_cache_slot's checks,
+ * d not in {64, 128}, null or aliased pointers).
+ */
+int kv_cache_rope(const void* cache_k, void* k_rot, const float* rope_angles,
+                  int B, int Hkv, int d, int chunk_len, int sink_size, int window_size,
+                  int64_t chunk_idx, int rope_style, void* stream);
 
 /*
  * attn_forward -- scaled dot-product attention forward pass, bf16 in and out.

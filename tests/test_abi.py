@@ -77,8 +77,12 @@ def test_qk_norm_rope_rejects_bad_arguments():
     g = ctypes.c_void_p(8192)
     # head dim not built
     assert L.qk_norm_rope(P, P, 96 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 96, 1e-6, 1, 1, None) == -3
-    # inner scope is not built
-    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 2, 1, None) == -3
+    # inner scope with grouped key heads
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, P, P, 128 * 2 * 4, g, g, g, 1, 4, 8, 2, 128, 1e-6, 2, 1, None) == -3
+    # unknown norm scope; the after-cache flag without a pairing; pairing value 3
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 3, 1, None) == -3
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 1, 4, None) == -3
+    assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 1, 7, None) == -3
     # RoPE enabled without angles
     assert L.qk_norm_rope(P, P, 128 * 8 * 4, None, None, 0, g, None, None, 1, 4, 8, 0, 128, 1e-6, 1, 1, None) == -1
     # head norm without weights
@@ -136,3 +140,35 @@ def test_attn_forward_window_rejects_bad_arguments(left, right, Lq, Lk, code):
 def test_attn_forward_window_accepts_lq_up_to_lk_plus_right():
     # Lq = Lk + right passes shape validation; the null q pointer is what stops the call
     assert _win(-1, 4, 20, 16, q=None) == -1
+
+
+@pytest.mark.parametrize("Lc,sink,window", [(1785, 0, 7140), (10, 10, 30), (10, 20, 10), (3, 0, 3), (7, 14, 35)])
+def test_kv_cache_positions_match_oracle_arrival_order(Lc, sink, window):
+    """Physical row -> logical row of the visible keys, against the oracle's chunk simulation:
+    the logical order is the visible chunks in arrival order (sinks first)."""
+    model = RollingCacheModel(Lc, sink, window)
+    for c in range(2 * (sink + window) // Lc + 7):
+        model.write(c)
+        pos = binding.kv_cache_positions(c, Lc, sink, window)
+        vis = model.visible_chunks()
+        assert len(pos) == model.visible_len()
+        expect = [0] * len(pos)
+        for logical_chunk, chunk in enumerate(vis):
+            s0 = model.slot_of(chunk)
+            for i in range(Lc):
+                expect[s0 + i] = logical_chunk * Lc + i
+        assert pos == expect, (c, pos[:: max(1, Lc)], expect[:: max(1, Lc)])
+
+
+def test_kv_cache_rope_rejects_bad_arguments():
+    L = lib()
+    P, Q = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert L.kv_cache_rope(P, Q, P, 1, 4, 128, 16, 0, 64, 0, 3, None) == -3      # pairing
+    assert L.kv_cache_rope(P, Q, P, 1, 4, 128, 16, 0, 64, 0, 0, None) == -3      # no rotation
+    assert L.kv_cache_rope(P, Q, P, 1, 4, 96, 16, 0, 64, 0, 1, None) == -3       # head dim
+    assert L.kv_cache_rope(P, P, P, 1, 4, 128, 16, 0, 64, 0, 1, None) == -2      # in place
+    assert L.kv_cache_rope(P, Q, None, 1, 4, 128, 16, 0, 64, 0, 1, None) == -1   # no angles
+    assert L.kv_cache_rope(P, Q, P, 1, 4, 128, 16, 8, 64, 0, 1, None) == -5      # sink not a multiple
+    assert L.kv_cache_rope(P, Q, P, 1, 0, 128, 16, 0, 64, 0, 1, None) == -5      # no heads
+    out = (ctypes.c_int64 * 4)()
+    assert L.kv_cache_positions(5, 16, 0, 64, out, 4) == -5                      # output too small

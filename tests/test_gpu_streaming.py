@@ -14,10 +14,16 @@ DEV = "cuda"
 SENTINEL = 0x7E11  # a bf16 NaN pattern no copy produces
 
 
-def _oracle_prologue(x, gamma, eps, angles, style):
+def _oracle_prologue(x, gamma, eps, angles, style, inner=False):
+    """Oracle RMSNorm (head scope, or inner scope over all heads of a token) then RoPE, fp64."""
     g = None if gamma is None else gamma.double().numpy()
     a = None if angles is None else angles.double().numpy()
-    return oracle.qk_norm_rope(widen(x).reshape(x.shape), g, eps, a, style)
+    z = widen(x).reshape(x.shape)
+    if inner and g is not None:
+        B, L, H, d = x.shape
+        z = oracle.rmsnorm(z.reshape(B, L, H * d), g, eps).reshape(B, L, H, d)
+        g = None
+    return oracle.qk_norm_rope(z, g, eps, a, style)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -40,6 +46,72 @@ def test_qk_norm_rope_matches_oracle(d, style, with_k):
     assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, style), "q")
     if with_k:
         assert_within_one_ulp(ko, _oracle_prologue(k, gk, 1e-6, ang, style), "k")
+
+
+@pytest.mark.parametrize("d,H,with_k", [(128, 5, True), (64, 5, True), (128, 7, False), (128, 80, True),
+                                         (64, 150, True)])
+def test_qk_norm_rope_inner_scope(d, H, with_k):
+    """Inner-scope RMSNorm (m = H*d over all heads of a token) then split RoPE. H*2 rows above 128
+    (d = 128) or 256 (d = 64) exercise the path that reads the rows twice."""
+    B, L = 2, 9
+    print(f"[case] inner d={d} H={H} with_k={with_k}", flush=True)
+    g = torch.Generator().manual_seed(200 + d + H)
+    q = synthetic.normal((B, L, H, d), "bf16", g, 2.0)
+    k = synthetic.normal((B, L, H, d), "bf16", g, 0.5)
+    gq, gk = synthetic.norm_weight(H * d, g), synthetic.norm_weight(H * d, g)
+    ang = synthetic.rope_angles(np.arange(300, 300 + L), d)
+    qd, kd = q.to(DEV), k.to(DEV)
+    qo = torch.empty_like(qd)
+    ko = torch.empty_like(kd) if with_k else None
+    binding.qk_norm_rope(qd, qo, kd if with_k else None, ko, gq.to(DEV), gk.to(DEV) if with_k else None,
+                         ang.to(DEV), 1e-6, binding.SA_NORM_INNER, binding.SA_ROPE_SPLIT)
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, oracle.SPLIT, inner=True), "q inner")
+    if with_k:
+        assert_within_one_ulp(ko, _oracle_prologue(k, gk, 1e-6, ang, oracle.SPLIT, inner=True), "k inner")
+
+
+@pytest.mark.parametrize("style", [binding.SA_ROPE_SPLIT, binding.SA_ROPE_INTERLEAVED])
+def test_qk_norm_rope_after_cache_rotates_queries_only(style):
+    B, L, Hq, Hkv, d = 1, 33, 4, 2, 128
+    g = torch.Generator().manual_seed(17 + style)
+    q = synthetic.normal((B, L, Hq, d), "bf16", g)
+    k = synthetic.normal((B, L, Hkv, d), "bf16", g)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    ang = synthetic.rope_angles(np.arange(40, 40 + L), d)
+    qd, kd = q.to(DEV), k.to(DEV)
+    qo, ko = torch.empty_like(qd), torch.empty_like(kd)
+    binding.qk_norm_rope(qd, qo, kd, ko, gq.to(DEV), gk.to(DEV), ang.to(DEV), 1e-6, binding.SA_NORM_HEAD,
+                         style | binding.SA_ROPE_AFTER_CACHE)
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, style), "q rotated")
+    assert_within_one_ulp(ko, _oracle_prologue(k, gk, 1e-6, None, 0), "k normalised only")
+
+
+@pytest.mark.parametrize("Lc,sink,window,chunk,d", [(40, 40, 120, 6, 128), (40, 0, 120, 1, 128), (32, 64, 64, 7, 64)])
+def test_kv_cache_rope_matches_oracle(Lc, sink, window, chunk, d):
+    """Every visible cache row rotated with the angles of its arrival-order row (from the oracle's
+    cache simulation); rows past the visible length untouched."""
+    B, H = 2, 3
+    S = sink + window
+    model = RollingCacheModel(Lc, sink, window)
+    for c in range(chunk + 1):
+        model.write(c)
+    n = model.visible_len()
+    g = torch.Generator().manual_seed(Lc + chunk)
+    cache = synthetic.normal((B, S, H, d), "bf16", g)
+    ang = synthetic.rope_angles(np.arange(n) * 3 + 11, d)
+    k_rot = torch.full((B, S, H, d), 0, dtype=torch.int16).fill_(SENTINEL).view(torch.bfloat16).to(DEV)
+    binding.kv_cache_rope(cache.to(DEV), k_rot, ang.to(DEV), chunk, Lc, sink, window, binding.SA_ROPE_SPLIT)
+    torch.cuda.synchronize()
+    got = k_rot.cpu()
+    logical = np.empty(n, dtype=np.int64)
+    for j, x in enumerate(model.visible_chunks()):
+        s0 = model.slot_of(x)
+        logical[s0:s0 + Lc] = j * Lc + np.arange(Lc)
+    ref = oracle.rope(widen(cache[:, :n]).reshape(B, n, H, d), ang.double().numpy()[logical], oracle.SPLIT)
+    assert_within_one_ulp(got[:, :n], ref, "k_rot")
+    assert bool((got[:, n:].view(torch.int16) == SENTINEL).all()), "rows past the visible length were written"
 
 
 def test_qk_norm_rope_without_norm_and_in_place():
@@ -101,14 +173,22 @@ def test_kv_cache_append_bit_exact_fill_and_eviction(B, Lc, H, d, sink, window):
         assert torch.equal(cache_v.cpu(), expect_v), f"V cache differs after chunk {c}"
 
 
-def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, style=binding.SA_ROPE_SPLIT):
-    """Run the streaming loop on the GPU and compare every chunk's output with the oracle."""
+def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, style=binding.SA_ROPE_SPLIT,
+                   after_cache=False, inner=False):
+    """Run the streaming loop on the GPU and compare every chunk's output with the oracle.
+
+    Before-cache RoPE: angles at absolute stream positions c*Lc + i rotate the chunk's queries
+    and keys, and the cache stores rotated keys. After-cache RoPE: the cache stores normalised,
+    unrotated keys; each step rotates the visible keys at their rows 0 .. n-1 of the visible
+    sequence (arrival order) and the queries at the last Lc rows."""
     eps, scale = 1e-6, d ** -0.5
-    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV)
+    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after_cache)
     model = RollingCacheModel(Lc, sink, window)
     g = torch.Generator().manual_seed(seed0)
-    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    gdim = H * d if inner else d
+    gq, gk = synthetic.norm_weight(gdim, g), synthetic.norm_weight(gdim, g)
     gqd, gkd = gq.to(DEV), gk.to(DEV)
+    scope = binding.SA_NORM_INNER if inner else binding.SA_NORM_HEAD
     kstar, vals = {}, {}
     results = []
     for c in range(n_chunks):
@@ -116,20 +196,27 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
         q = synthetic.normal((B, Lc, H, d), "bf16", gc)
         k = synthetic.normal((B, Lc, H, d), "bf16", gc)
         v = synthetic.normal((B, Lc, H, d), "bf16", gc)
-        ang = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d)
+        model.write(c)
+        n = model.visible_len()
+        if after_cache:
+            ang = synthetic.rope_angles(np.arange(n), d)       # rows of the visible sequence
+            ang_q = ang[n - Lc:]
+        else:
+            ang = ang_q = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d)
         q_buf = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
         out = torch.empty_like(q_buf)
         vis_len = binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, gqd, gkd,
-                                                     ang.to(DEV), eps, scale, style)
+                                                     ang.to(DEV), eps, scale, style, scope)
         torch.cuda.synchronize()
         # oracle: prologue in fp64, rounded once to the bf16 the cache stores; logical window
-        qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang, style), "bf16")
-        kstar[c] = oracle.round_to(_oracle_prologue(k, gk, eps, ang, style), "bf16")
+        qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang_q, style, inner), "bf16")
+        kstar[c] = oracle.round_to(_oracle_prologue(k, gk, eps, None if after_cache else ang, style, inner), "bf16")
         vals[c] = widen(v).reshape(v.shape)
-        model.write(c)
         vis = model.visible_chunks()
-        assert vis_len == model.visible_len()
+        assert vis_len == n
         K = np.concatenate([kstar[x] for x in vis], axis=1)
+        if after_cache:  # rotated visible keys enter attention as bf16, like the cache's keys
+            K = oracle.round_to(oracle.rope(K, ang.double().numpy(), style), "bf16")
         V = np.concatenate([vals[x] for x in vis], axis=1)
         if rows_per_chunk is None:
             ref = oracle.attention(qs, K, V, scale)
@@ -153,6 +240,38 @@ def test_streaming_small_with_sink_full_compare():
 def test_streaming_interleaved_rope_d64():
     _streaming_run(B=1, Lc=64, H=3, d=64, sink=0, window=192, n_chunks=5, rows_per_chunk=None, seed0=4100,
                    style=binding.SA_ROPE_INTERLEAVED)
+
+
+def test_streaming_after_cache_rope_with_sink():
+    # after-cache RoPE, sink 1 chunk + window 3 chunks: fill and evictions; the sink's position
+    # moves next to the window each step
+    _streaming_run(B=2, Lc=100, H=4, d=128, sink=100, window=300, n_chunks=8, rows_per_chunk=None, seed0=4200,
+                   after_cache=True)
+
+
+def test_streaming_after_cache_interleaved_d64_no_sink():
+    _streaming_run(B=1, Lc=64, H=3, d=64, sink=0, window=192, n_chunks=5, rows_per_chunk=None, seed0=4300,
+                   style=binding.SA_ROPE_INTERLEAVED, after_cache=True)
+
+
+def test_streaming_inner_scope_norm():
+    # inner-scope Q/K RMSNorm (one RMS over all heads of a token), before-cache RoPE
+    _streaming_run(B=1, Lc=96, H=6, d=128, sink=0, window=288, n_chunks=4, rows_per_chunk=None, seed0=4400,
+                   inner=True)
+
+
+def test_streaming_inner_scope_after_cache_d64():
+    _streaming_run(B=2, Lc=50, H=4, d=64, sink=50, window=100, n_chunks=5, rows_per_chunk=None, seed0=4500,
+                   inner=True, after_cache=True)
+
+
+def test_streaming_after_cache_full_size_with_sink():
+    """After-cache RoPE at full size: chunks of 1785 tokens x 40 heads x 128, cache of one sink
+    chunk + a 3-chunk window (7140 keys), chunks 0-5 (fill, then eviction); sampled rows."""
+    w = synthetic.WORKLOADS["stream_self_1785x4"]
+    print(f"[case] after-cache {w}", flush=True)
+    _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=w.chunk, window=w.window - w.chunk, n_chunks=6,
+                   rows_per_chunk=512, seed0=w.seed + 50, after_cache=True)
 
 
 def test_streaming_self_attention_full_size():

@@ -363,3 +363,50 @@ def test_window_two_keys_sigmoid():
         np.testing.assert_allclose(out[0, i, 0], w_cur * v[0, i, 0] + (1.0 - w_cur) * v[0, i - 1, 0],
                                    rtol=0, atol=1e-13)
     np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 0], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ after-cache RoPE positions
+
+def _angles64(positions, d):
+    p = np.asarray(positions, dtype=np.float64)[:, None]
+    return p * np.power(10000.0, -2.0 * np.arange(d // 2)[None, :] / d)
+
+
+def _after_vs_before(Lc, sink, window, n_chunks, d=8, H=2, seed=0):
+    from oracle.cache import RollingCacheModel
+    rng = np.random.default_rng(seed)
+    model = RollingCacheModel(Lc, sink, window)
+    keys, vals = {}, {}
+    for c in range(n_chunks):
+        keys[c] = rng.standard_normal((1, Lc, H, d))
+        vals[c] = rng.standard_normal((1, Lc, H, d))
+        model.write(c)
+    c = n_chunks - 1
+    q = rng.standard_normal((1, Lc, H, d))
+    vis = model.visible_chunks()
+    K = np.concatenate([keys[x] for x in vis], axis=1)
+    V = np.concatenate([vals[x] for x in vis], axis=1)
+    # before-cache: keys keep the absolute stream positions they were written at
+    abs_pos = np.concatenate([np.arange(x * Lc, (x + 1) * Lc) for x in vis])
+    before = oracle.attention(oracle.rope(q, _angles64(np.arange(c * Lc, (c + 1) * Lc), d), oracle.SPLIT),
+                              oracle.rope(K, _angles64(abs_pos, d), oracle.SPLIT), V, 0.3)
+    # after-cache: every visible key at its row of the visible sequence, queries at the last Lc rows
+    n = model.visible_len()
+    after = oracle.attention(oracle.rope(q, _angles64(np.arange(n - Lc, n), d), oracle.SPLIT),
+                             oracle.rope(K, _angles64(np.arange(n), d), oracle.SPLIT), V, 0.3)
+    return before, after
+
+
+def test_after_cache_positions_equal_absolute_without_sinks():
+    """RoPE scores depend only on position differences. Without sinks the visible window is a
+    contiguous run of the stream, so cache-relative positions (after-cache RoPE) give the same
+    attention as absolute positions (before-cache RoPE)."""
+    before, after = _after_vs_before(Lc=4, sink=0, window=12, n_chunks=6)
+    np.testing.assert_allclose(after, before, rtol=0, atol=1e-12)
+
+
+def test_after_cache_positions_close_the_gap_after_a_sink():
+    """With a sink chunk and evictions the sink sits right before the window in cache-relative
+    positions, far from it in absolute ones: the two readings must differ."""
+    before, after = _after_vs_before(Lc=4, sink=4, window=8, n_chunks=6)
+    assert np.abs(after - before).max() > 1e-3
