@@ -7,10 +7,11 @@
 // running row maximum m and row sum l are kept in registers, and the partial output is
 // rescaled by exp2(m_old - m_new) whenever the maximum grows. No score matrix is stored.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one (batch, head)):
+// Work decomposition (one workgroup = 128 or 256 query rows of one (batch, head)):
 //   * each wave owns 32 query rows; its Q^T slice stays in registers as the MFMA B operand;
-//   * K and V tiles of 64 keys are staged global -> registers -> LDS, double buffered, so the
-//     next tile's global loads are in flight while the current tile is computed;
+//   * K and V tiles of 32 or 64 keys are staged global -> registers -> LDS, double buffered, so
+//     the next tile's global loads are in flight while the current tile is computed; an 8-wave
+//     workgroup may instead split the keys between two groups of 4 waves, merged at the end;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16 (bf16 or f16): each lane then holds 16 scores of ONE
 //     query column, so row max/sum are in-lane reductions plus one v_permlane32_swap;
 //   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16: the score registers, converted to f16, are
@@ -106,18 +107,22 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 // Launch shapes. Every wave owns 32 query rows and every lane stays within 256 registers, so
 // two waves share each SIMD:
-//   NW = 8 waves (256 query rows) per workgroup, one workgroup per CU, 64-key tiles: K/V tiles
-//     are staged once for 256 rows, so each thread converts and stores half as much;
-//   NW = 4 waves (128 rows), two workgroups per CU: twice as many workgroups, for grids that
-//     would otherwise leave CUs idle. Keys per tile: 32 for d = 128, 64 for d = 64.
-template <int D, int NW>
-constexpr int tile_keys() { return (NW == 4 && D == 128) ? 32 : 64; }
+//   8 waves, one key group (256 query rows) per workgroup, one workgroup per CU, 64-key tiles:
+//     K/V tiles are staged once for 256 rows, so each thread converts and stores half as much;
+//   4 waves (128 rows), two workgroups per CU: twice as many workgroups, for grids that would
+//     otherwise leave CUs idle;
+//   8 waves as two key groups of 4 (128 rows, each group half of the keys): for grids with at
+//     most one 128-row workgroup per CU.
+// Keys per tile for a group of RW row waves: 32 for d = 128 with 4 row waves, 64 otherwise.
+template <int D, int RW>
+constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 
-template <int D, bool BF16, int NW>
+template <int D, bool BF16, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
-    constexpr int kThreads = NW * 64;
-    constexpr int kBM = NW * 32;  // query rows per workgroup
-    constexpr int kBN = tile_keys<D, NW>();
+    constexpr int kRW = NW / KS;          // row waves per key group
+    constexpr int kGThreads = kRW * 64;   // threads of one key group (they stage its tiles)
+    constexpr int kBM = kRW * 32;         // query rows per workgroup
+    constexpr int kBN = tile_keys<D, kRW>();
     constexpr int KB = kBN / 32;  // 32-key score blocks per tile
     constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
     constexpr int KST = D + 8;    // LDS row stride of a K tile (elements): conflict-free b128 reads
@@ -125,16 +130,22 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr int DC = D / 16;    // QK MFMAs per 32-key block (16 features each)
     constexpr int DB = D / 32;    // 32-feature blocks of the O^T accumulator
     constexpr int CPR = D / 8;    // 16-byte chunks per key row
-    constexpr int NCH = kBN * CPR / kThreads;  // 16-byte chunks each thread stages per tile
-    constexpr int RSTEP = kThreads / CPR;      // key rows between a thread's chunks
-    static_assert(NCH * kThreads == kBN * CPR, "tile must split evenly over the workgroup");
+    constexpr int NCH = kBN * CPR / kGThreads;  // 16-byte chunks each thread stages per tile
+    constexpr int RSTEP = kGThreads / CPR;      // key rows between a thread's chunks
+    static_assert(NCH * kGThreads == kBN * CPR, "tile must split evenly over the key group");
+    static_assert(KS == 1 || KS == 2, "one or two key groups");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KST];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VST];
+    // Each key group owns two K slots and two V slots (double buffering) in LDS. K and V are
+    // separate arrays so every LDS offset stays within the 16-bit immediate of ds_read/ds_write.
+    constexpr int kKSlot = kBN * KST, kVSlot = kBN * VST;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KS][2 * kKSlot];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KS][2 * kVSlot];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int ks = KS == 1 ? 0 : wave / kRW;     // key group of this wave
+    const int rw = KS == 1 ? wave : wave % kRW;  // row wave within the group
     const int g = lane >> 5;   // half of the wave
     const int j = lane & 31;   // query column owned by this lane
 
@@ -153,7 +164,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     const int hk = h / p.group;
 
     const int qb0 = qblk * kBM;
-    const int r0 = qb0 + wave * 32;  // this wave's first query row
+    const int r0 = qb0 + rw * 32;    // this wave's first query row
     const int qrow = r0 + j;
     const int shift = p.Lk - p.Lq;   // query i sits at key position i + shift
     const int qlast = min(qb0 + kBM, p.Lq) - 1;
@@ -169,6 +180,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     if (p.win_left >= 0) tl = max(t0, (qlast + shift - p.win_left + kBN - 1) / kBN);
     int tr = p.Lk / kBN;
     if (p.win_right >= 0) tr = min(tr, max(0, (qb0 + shift + p.win_right + 1) / kBN));
+    // Key groups split [t0, nkt) into consecutive runs of nsteps tiles; every group runs the same
+    // number of steps (they share the barriers), so the last group may step over tiles >= nkt:
+    // those re-read the last tile and are masked out entirely (tr <= nkt).
+    const int nsteps = KS == 1 ? nkt - t0 : (nkt - t0 + 1) / 2;
+    const int ta = t0 + ks * nsteps;
+    const int tend = KS == 1 ? nkt : ta + nsteps;
     // this lane's visible keys [key_lo, key_lo + key_span] (rows past Lq may get an empty or
     // wrapped range; their scores are never stored)
     int key_lo, key_hi;
@@ -189,11 +206,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 
     // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, features
     // scol..scol+7) of every tile; rows past Lk re-read row Lk - 1 (their scores are masked).
-    const int srow0 = tid / CPR, scol = (tid % CPR) * 8;
+    const int tid_g = KS == 1 ? tid : tid % kGThreads;
+    const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * 8;
     const uint16_t* kg = p.k + b * p.kv_bstride + hk * D + scol;
     const uint16_t* vg = p.v + b * p.kv_bstride + hk * D + scol;
-    uint16_t* ks_st = &Ks[0][srow0 * KST + scol];
-    uint16_t* vs_st = &Vs[0][srow0 * VST + scol];
+    uint16_t* const Kg = &Ks[ks][0];  // this group's K and V slots
+    uint16_t* const Vg = &Vs[ks][0];
+    uint16_t* ks_st = Kg + srow0 * KST + scol;
+    uint16_t* vs_st = Vg + srow0 * VST + scol;
     u32x4 kreg[NCH], vreg[NCH];
     auto load_k = [&](int kt) __attribute__((always_inline)) {
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
@@ -221,11 +241,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 
     // LDS read addresses (address space 3, so constant offsets fold into the instructions).
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
-    lds_u4* kq_lane = (lds_u4*)(&Ks[0][j * KST + 8 * g]);
+    lds_u4* kq_lane = (lds_u4*)(Kg + j * KST + 8 * g);
     // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
     // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
     const int G = lane >> 4, L16 = lane & 15;
-    lds_i16x4* v_lane = (lds_i16x4*)(&Vs[0][(4 * (G >> 1) + (L16 >> 2)) * VST + 16 * (G & 1) + 4 * (L16 & 3)]);
+    lds_i16x4* v_lane = (lds_i16x4*)(Vg + (4 * (G >> 1) + (L16 >> 2)) * VST + 16 * (G & 1) + 4 * (L16 & 3));
 
     const float c = p.c;
     // Running maximum used as the exponent offset (log2 domain). It is raised only when a
@@ -350,28 +370,61 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         if (t < t1) step(T_{}, T_{}, do_mask, t, s0, s1);
     };
 
-    if (nkt > t0) {
-        load_k(t0);
-        store_k(t0 & 1);
-        load_k(min(t0 + 1, nkt - 1));
-        load_v(t0);
+    if (nkt > t0) {  // uniform over the workgroup: every group runs nsteps + 1 steps
+        load_k(ta);
+        store_k(ta & 1);
+        load_k(min(ta + 1, nkt - 1));
+        load_v(ta);
         __syncthreads();
-        const bool mask0 = t0 < tl || t0 >= tr;
-        if (t0 & 1) {
-            if (mask0) step(T_{}, F_{}, T_{}, t0, s1, s0);
-            else step(T_{}, F_{}, F_{}, t0, s1, s0);
+        const bool mask0 = ta < tl || ta >= tr;
+        if (ta & 1) {
+            if (mask0) step(T_{}, F_{}, T_{}, ta, s1, s0);
+            else step(T_{}, F_{}, F_{}, ta, s1, s0);
         } else {
-            if (mask0) step(T_{}, F_{}, T_{}, t0, s0, s1);
-            else step(T_{}, F_{}, F_{}, t0, s0, s1);
+            if (mask0) step(T_{}, F_{}, T_{}, ta, s0, s1);
+            else step(T_{}, F_{}, F_{}, ta, s0, s1);
         }
-        // steps t0+1 .. nkt-1 in three segments: left-edge masked, unmasked, right-edge masked
-        const int e1 = min(max(tl, t0 + 1), nkt);
-        const int e2 = max(e1, min(tr, nkt));
-        middle(T_{}, t0 + 1, e1);
+        // steps ta+1 .. tend-1 in three segments: left-edge masked, unmasked, right-edge masked
+        const int e1 = min(max(tl, ta + 1), tend);
+        const int e2 = max(e1, min(tr, tend));
+        middle(T_{}, ta + 1, e1);
         middle(F_{}, e1, e2);
-        middle(T_{}, e2, nkt);
-        if (nkt & 1) step(F_{}, T_{}, F_{}, nkt, s1, s0);  // S(nkt-1) in s0 when nkt-1 is even
-        else step(F_{}, T_{}, F_{}, nkt, s0, s1);
+        middle(T_{}, e2, tend);
+        if (tend & 1) step(F_{}, T_{}, F_{}, tend, s1, s0);  // S(tend-1) in s0 when tend-1 is even
+        else step(F_{}, T_{}, F_{}, tend, s0, s1);
+    }
+
+    if constexpr (KS == 2) {
+        // Merge the two key groups' partial results through LDS (the tiles are no longer read:
+        // every step ended with a barrier): (m, l, O) = (max, l0 a0 + l1 a1, O0 a0 + O1 a1) with
+        // a_i = exp2(m_i - m). Group 1 hands over -- the first half of O in the K buffers, the
+        // rest with m and l in the V buffers -- and group 0 merges and stores.
+        constexpr int NA = 16 * (DB / 2), NB = 16 * (DB - DB / 2) + 2;
+        static_assert(kRW * NA * 64 * 4 <= (int)sizeof(Ks) && kRW * NB * 64 * 4 <= (int)sizeof(Vs),
+                      "merge area must fit in the tile buffers");
+        float* mrg_a = reinterpret_cast<float*>(&Ks[0][0]) + rw * NA * 64 + lane;
+        float* mrg_b = reinterpret_cast<float*>(&Vs[0][0]) + rw * NB * 64 + lane;
+        auto slot = [&](int db, int r) __attribute__((always_inline)) -> float* {
+            return db < DB / 2 ? mrg_a + (16 * db + r) * 64 : mrg_b + (16 * (db - DB / 2) + r) * 64;
+        };
+        if (ks == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) *slot(db, r) = o[db][r];
+            mrg_b[(NB - 2) * 64] = m_run;
+            mrg_b[(NB - 1) * 64] = l_run;
+        }
+        __syncthreads();
+        if (ks == 1) return;
+        const float m1 = mrg_b[(NB - 2) * 64], l1 = mrg_b[(NB - 1) * 64];
+        const float mn = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + *slot(db, r) * a1;
+        l_run = l_run * a0 + l1 * a1;
     }
 
     // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
@@ -413,9 +466,9 @@ int device_cu_count() {
     return cached_cus;
 }
 
-template <int D, bool BF16, int NW>
+template <int D, bool BF16, int NW, int KS>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-    constexpr int kBM = NW * 32;
+    constexpr int kBM = NW / KS * 32;
     KParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -436,18 +489,25 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     const int64_t nblocks = (int64_t)p.n_qblk * a.Hq * a.B;
     p.nblocks = (int)nblocks;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, NW, KS>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
-    // 256-row workgroups when there are at least four per CU (long sequences); 128-row ones
-    // otherwise, where twice as many workgroups fill the CUs better (measured on MI355X: the
-    // 40-head, 1785-query workloads run faster with 128 rows, 56 heads x 20480 with 256).
+    // 256-row workgroups when there are at least four per CU (long sequences). Otherwise 128-row
+    // workgroups of 4 waves, two per CU -- unless even those leave CUs with a single 4-wave
+    // workgroup (at most one per CU) over a long key loop: then 8 waves split the keys in two
+    // halves, so every CU runs 8 waves on half as many keys each. Measured on MI355X: the split
+    // pays for [2, 2048, 8, 64] causal (256 workgroups, +15 %), but not for grids above one
+    // workgroup per CU (the shared barriers of the two halves cost more than the finer
+    // balancing gains) nor for loops of a few tiles (the merge does not amortise).
+    const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
-    if (wg256 >= 4 * (int64_t)device_cu_count()) return launch<D, BF16, 8>(a, stream);
-    return launch<D, BF16, 4>(a, stream);
+    if (wg256 >= 4 * cus) return launch<D, BF16, 8, 1>(a, stream);
+    const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
+    if (wg128 <= cus && a.Lk >= 512) return launch<D, BF16, 8, 2>(a, stream);
+    return launch<D, BF16, 4, 1>(a, stream);
 }
 
 }  // namespace

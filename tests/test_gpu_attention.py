@@ -158,3 +158,44 @@ def test_attention_wide_grid_sampled_rows(case):
     ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
                            d ** -0.5, causal, rows=rows)
     assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name)
+
+
+def _shape_cases():
+    """Shapes that land in each launch regime for this device's CU count: 8-wave workgroups with
+    the keys split in two (at most one 128-row block per CU and at least 512 keys), 4-wave
+    workgroups (short key loops, or between one and four 128-row blocks per CU)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks4 = (3 * cus) // 2          # 128-row blocks: 1.5 per CU -> 4-wave workgroups
+    H4 = 64
+    Lq4 = -(-blocks4 // H4) * 128 - 37
+    return [
+        # name, B, Lq, Lk, Hq, Hkv, d, dtype, causal, window
+        ("split_ragged_bf16_d128", 1, 300, 1111, 4, 2, 128, "bf16", False, None),
+        ("split_causal_f16_d64", 2, 600, 600, 3, 3, 64, "f16", True, None),
+        ("short_keys_bf16_d128", 1, 100, 20, 2, 2, 128, "bf16", False, None),
+        ("split_odd_tiles_bf16_d128", 2, 129, 513, 3, 1, 128, "bf16", False, None),
+        ("split_window_bf16_d128", 1, 700, 700, 2, 2, 128, "bf16", False, (100, 30)),
+        ("wave4_bf16_d128", 1, Lq4, 900, H4, 16, 128, "bf16", False, None),
+        ("wave4_causal_f16_d64", 1, Lq4, Lq4, H4, H4, 64, "f16", True, None),
+        ("wave4_window_bf16_d128", 1, Lq4, Lq4 + 50, H4, 8, 128, "bf16", False, (200, 0)),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_launch_regimes_sampled_rows(idx):
+    name, B, Lq, Lk, Hq, Hkv, d, dtype, causal, window = _shape_cases()[idx]
+    print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} window={window}",
+          flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 10000)
+    scale = d ** -0.5
+    if window is None:
+        out = _run(q, k, v, scale, causal, dtype)
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        out = torch.empty_like(qd)
+        binding.attn_forward_window(qd, kd, vd, out, scale, window)
+        torch.cuda.synchronize()
+    rows = sample_rows(B, Lq, Hq, 3000, seed=idx)
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
+                           scale, causal, rows=rows, window=window)
+    assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name)
