@@ -21,11 +21,11 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16, "e4m3": torch.float8_e4m3fn}
 
 
 def normal(shape, dtype: str, gen: torch.Generator, scale: float = 1.0) -> torch.Tensor:
-    """fp32 N(0, 1) * scale, cast to the 16-bit dtype (CPU tensor)."""
+    """fp32 N(0, 1) * scale, cast to the dtype (CPU tensor; e4m3 = unscaled float8_e4m3fn)."""
     x = torch.randn(tuple(shape), generator=gen, dtype=torch.float32)
     if scale != 1.0:
         x = x * scale
@@ -57,7 +57,9 @@ def rope_angles(positions, d: int, base: float = 10000.0) -> torch.Tensor:
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw 16-bit patterns of a CPU bf16/f16 tensor as a uint16 numpy array."""
+    """Raw bit patterns of a CPU tensor: uint16 for bf16/f16, uint8 for float8_e4m3fn."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.contiguous().view(torch.uint8).numpy()
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 

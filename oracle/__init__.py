@@ -19,6 +19,8 @@ section "Multi Head Attention Definition", unless stated otherwise:
                      "optimizing-attention-flash" (section "Step 3: Enable advanced features").
 * ``round_to``    -- round-to-nearest-even into bfloat16 / IEEE binary16, from the formats'
                      definitions, applied once to an fp64 value.
+* ``decode``      -- exact widening of bfloat16, binary16 and OCP FP8 E4M3 (float8_e4m3fn, the
+                     unscaled FP8 the quantized-SDPA option of the same page casts Q/K/V to).
 * ``cache``       -- the rolling sink + window K/V cache of the page's "Generic Multi Head
                      Attention Interface" section, simulated chunk by chunk (see cache.py).
 
@@ -65,6 +67,7 @@ def _load():
         D = ctypes.c_double
         lib.oracle_decode_bf16.argtypes = [P, P, I64]
         lib.oracle_decode_f16.argtypes = [P, P, I64]
+        lib.oracle_decode_e4m3.argtypes = [P, P, I64]
         lib.oracle_rmsnorm.argtypes = [P, P, P, I64, I, D]
         lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I]
         lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I]
@@ -88,7 +91,13 @@ def default_threads() -> int:
 # ------------------------------------------------------------------ 16-bit formats
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Widen 16-bit float bit patterns (uint16/int16 array) exactly to float64."""
+    """Widen float bit patterns exactly to float64: 16-bit patterns (uint16/int16) for "bf16" and
+    "f16", 8-bit patterns (uint8/int8) for "e4m3" (OCP FP8 E4M3, the float8_e4m3fn format)."""
+    if dtype == "e4m3":
+        b = np.ascontiguousarray(bits).view(np.uint8)
+        out = np.empty(b.shape, dtype=np.float64)
+        _load().oracle_decode_e4m3(_ptr(b), _ptr(out), b.size)
+        return out
     b = np.ascontiguousarray(bits).view(np.uint16)
     out = np.empty(b.shape, dtype=np.float64)
     fn = {"bf16": _load().oracle_decode_bf16, "f16": _load().oracle_decode_f16}[dtype]

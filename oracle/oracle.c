@@ -7,7 +7,8 @@
  *
  * Every function restates a definition from the page "flashdreams.accelerated" (developer
  * guide), section "Multi Head Attention Definition":
- *   - 16-bit float decoding is the IEEE-754 binary16 / bfloat16 bit-format definition;
+ *   - 16-bit float decoding is the IEEE-754 binary16 / bfloat16 bit-format definition, and 8-bit
+ *     decoding the OCP FP8 E4M3 definition;
  *   - RMSNorm: gamma (.) z / sqrt(mean(z^2) + eps), the RMSNorm equation of that section;
  *   - RoPE: the 2x2 rotation of pair r by angle theta_{p,r} (rotation equation), with the
  *     split-half pairs (r, r + d/2) or interleaved pairs (2r, 2r + 1) named there;
@@ -48,6 +49,29 @@ static double decode_f16_one(uint16_t h) {
     else
         mag = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/1024) * 2^(expo-15) */
     return sign ? -mag : mag;
+}
+
+/* FP8 E4M3 in the OCP 8-bit floating-point format ("e4m3fn"): 1 sign bit, 4 exponent bits
+ * (bias 7), 3 fraction bits; exponent 0 holds subnormals frac * 2^-9; there is no infinity, and
+ * only exponent 15 with fraction 7 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ * This is the unscaled float8_e4m3fn the page "flashdreams.accelerated" (section
+ * OptimizedMultiHeadAttention, quantized SDPA option) casts Q, K and V to. */
+static double decode_e4m3_one(uint8_t x) {
+    int sign = (x >> 7) & 1;
+    int expo = (x >> 3) & 0xf;
+    int frac = x & 0x7;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -9);               /* frac/8 * 2^(1-7) */
+    else if (expo == 15 && frac == 7)
+        mag = NAN;
+    else
+        mag = ldexp((double)(8 + frac), expo - 10);  /* (1 + frac/8) * 2^(expo-7) */
+    return sign ? -mag : mag;
+}
+
+void oracle_decode_e4m3(const uint8_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_e4m3_one(in[i]);
 }
 
 void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n) {

@@ -15,8 +15,8 @@ ATTN_MEAN_ABS = 1e-4
 
 
 def widen(t: torch.Tensor) -> np.ndarray:
-    """Exact fp64 values of a CPU or GPU 16-bit tensor, decoded by the oracle from its bits."""
-    dt = "bf16" if t.dtype == torch.bfloat16 else "f16"
+    """Exact fp64 values of a CPU or GPU bf16/f16/float8_e4m3fn tensor, decoded by the oracle."""
+    dt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "e4m3"}[t.dtype]
     return oracle.decode(synthetic.bits(t.detach().cpu()), dt)
 
 

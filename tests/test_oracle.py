@@ -61,6 +61,21 @@ def test_decode_known_values():
     assert list(f) == [1.0, 65504.0, 2.0 ** -24, 0.333251953125, -4.0]
 
 
+def test_decode_e4m3_every_pattern_and_known_values():
+    """OCP FP8 E4M3 (float8_e4m3fn): all 256 codes against torch's float8_e4m3fn, and values
+    worked out from the format (bias 7, 3 fraction bits, subnormals, only S.1111.111 is NaN)."""
+    pats = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(pats, "e4m3")
+    ref = torch.from_numpy(pats.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert ((got == ref) | (np.isnan(got) & np.isnan(ref))).all()
+    known = {0x38: 1.0, 0x40: 2.0, 0xB8: -1.0, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x3C: 1.5, 0x33: 0.6875, 0x00: 0.0, 0x78: 256.0}
+    for code, value in known.items():
+        assert oracle.decode(np.array([code], dtype=np.uint8), "e4m3")[0] == value, hex(code)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.isfinite(got[[c for c in range(256) if c not in (0x7F, 0xFF)]]).all()  # no infinities
+
+
 def test_round_to_bf16_hand_cases():
     x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8 + 2 ** -30),
                   2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 0.0, -0.0, 3.0e38, 3.5e38])
