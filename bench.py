@@ -23,6 +23,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·Lq·Lk·d) and % of bf16 MFMA peak, 1×MI355X"
 PEAK_MFMA_16BIT = 2516.6   # TFLOP/s, dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_MFMA_FP8 = 5033.2     # TFLOP/s, dense FP8 MFMA (twice the 16-bit rate)
+# FP8 attention: Q K^T (half the flops) on FP8 MFMA, P V (the other half) on f16 MFMA
+PEAK_MFMA_FP8_F16 = 1.0 / (0.5 / PEAK_MFMA_FP8 + 0.5 / PEAK_MFMA_16BIT)
 PEAK_HBM = 8000.0          # GB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -83,6 +86,13 @@ def make_workload(name: str, dev: str):
     if w.prologue == "none":
         q, k, v = synthetic.attention_inputs(w.B, w.Lq, w.Lk, w.Hq, w.Hkv, w.d, w.dtype, w.seed)
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        if w.dtype == "e4m3":
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            info["compute"] = "Q K^T on FP8 E4M3 MFMA, P V on f16 MFMA, fp32 accumulation, bf16 out"
+
+            def step():
+                binding.attn_forward_fp8(q, k, v, out, w.scale, w.causal)
+            return w, step, step, info, (q, k, v)
         out = torch.empty_like(q)
         if w.attn_window is not None:
             info["window"] = list(w.attn_window)
@@ -299,6 +309,7 @@ def main():
         info["hbm_kernels"] = hbm
 
     flops = workload_flops(w)
+    peak = PEAK_MFMA_FP8_F16 if w.dtype == "e4m3" else PEAK_MFMA_16BIT
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kern * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
@@ -317,9 +328,9 @@ def main():
         "data": "synthetic",
         "config": dict(info, flops_per_step=flops, pct_of_bf16_peak=round(100 * value / PEAK_MFMA_16BIT, 2),
                        wall_ms_per_step=round(wall_ms, 4)),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_16BIT, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_MFMA_16BIT, 4), "traffic": traffic,
-                     "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'}>",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": f"attn_fwd_kernel<{w.d},{w.dtype}>",
                      "kernel_ms": round(ms_kern, 4)},
         "cpu_baseline": None,
     }

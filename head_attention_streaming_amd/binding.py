@@ -14,7 +14,7 @@ import torch
 
 from . import build as _build
 
-SA_DTYPE_BF16, SA_DTYPE_F16 = 0, 1
+SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3 = 0, 1, 2
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
 
@@ -78,6 +78,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return SA_DTYPE_BF16
     if t.dtype == torch.float16:
         return SA_DTYPE_F16
+    if t.dtype == torch.float8_e4m3fn:
+        return SA_DTYPE_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -99,8 +101,14 @@ def attn_forward_f16(q, k, v, out, scale: float, causal: bool = False):
     return out
 
 
+def attn_forward_fp8(q, k, v, out, scale: float, causal: bool = False):
+    """FP8 attention: q, k, v float8_e4m3fn (contiguous), out bf16 [B, Lq, Hq, d]."""
+    return attn_forward_kvstride(q, k, v, out, k.shape[1], scale, causal)
+
+
 def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = False):
-    """Attention over the first Lk tokens of k, v [B, S, Hkv, d] (S >= Lk), e.g. a rolling cache."""
+    """Attention over the first Lk tokens of k, v [B, S, Hkv, d] (S >= Lk), e.g. a rolling cache.
+    bf16/f16 tensors, or float8_e4m3fn q, k, v with a bf16 out."""
     B, Lq, Hq, d = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     kv_bstride = S * Hkv * d

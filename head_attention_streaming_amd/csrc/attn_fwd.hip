@@ -35,6 +35,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes as a native vector
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -42,11 +43,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Input element types (template parameter DT): bf16 or f16 (output in the same type), or FP8
+// E4M3 (OCP float8_e4m3fn, one byte; output bf16).
+constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2;
+
 struct KParams {
-    const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
-    uint16_t* out;
+    const void* q;  // [B, Lq, Hq, D] of the input type; strides below are in its elements
+    const void* k;
+    const void* v;
+    uint16_t* out;  // [B, Lq, Hq, D] bf16 (f16 for f16 input)
     int Hq, Hkv, Lq, Lk, group, n_qblk, nblocks;
     int win_left, win_right;  // visible keys of query i: [i+s-left, i+s+right], s = Lk-Lq; -1 = unbounded
     int64_t q_bstride, kv_bstride;
@@ -73,6 +78,27 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x) {
     r.z = pack_f16x2(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xffff0000u));
     r.w = pack_f16x2(__uint_as_float(x.w << 16), __uint_as_float(x.w & 0xffff0000u));
     return r;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// S^T block += K (32 keys x 64 features) * Q^T (64 features x 32 queries), FP8 E4M3 operands,
+// unit block scales (E8M0 exponent 127). Lane (g, i) holds features [32g, 32g + 32) of its row
+// in both operands (any feature order works if both operands use the same one).
+__device__ __forceinline__ f32x16 mfma_qk_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16 FP8 E4M3 values -> 16 f16 (exact: every E4M3 value is an f16 value)
+__device__ __forceinline__ uint32_t fp8x2_lo_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+__device__ __forceinline__ void fp8x16_to_f16x16(u32x4 x, u32x4& lo, u32x4& hi) {
+    lo = u32x4{fp8x2_lo_to_f16x2(x.x), fp8x2_hi_to_f16x2(x.x), fp8x2_lo_to_f16x2(x.y), fp8x2_hi_to_f16x2(x.y)};
+    hi = u32x4{fp8x2_lo_to_f16x2(x.z), fp8x2_hi_to_f16x2(x.z), fp8x2_lo_to_f16x2(x.w), fp8x2_hi_to_f16x2(x.w)};
 }
 
 template <bool BF16>
@@ -117,28 +143,38 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 template <int D, int RW>
 constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 
-template <int D, bool BF16, int NW, int KS>
+template <int D, int DT, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
+    constexpr bool FP8 = DT == kDtFP8;
+    constexpr bool BF16 = DT == kDtBF16;        // bf16 operands
+    constexpr bool OUT_BF16 = DT != kDtF16;      // bf16 output
+    using In = std::conditional_t<FP8, uint8_t, uint16_t>;
+    constexpr int EPC = FP8 ? 16 : 8;            // input elements per 16-byte chunk
     constexpr int kRW = NW / KS;          // row waves per key group
     constexpr int kGThreads = kRW * 64;   // threads of one key group (they stage its tiles)
     constexpr int kBM = kRW * 32;         // query rows per workgroup
     constexpr int kBN = tile_keys<D, kRW>();
     constexpr int KB = kBN / 32;  // 32-key score blocks per tile
     constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
-    constexpr int KST = D + 8;    // LDS row stride of a K tile (elements): conflict-free b128 reads
+    // LDS row stride of a K tile (input elements): 16 bytes of padding keep the b128 reads of
+    // 16 consecutive rows on distinct banks
+    constexpr int KST = D + 16 / (int)sizeof(In);
     constexpr int VST = D + 32;   // LDS row stride of a V tile: conflict-free transposed reads
-    constexpr int DC = D / 16;    // QK MFMAs per 32-key block (16 features each)
+    constexpr int DC = FP8 ? D / 64 : D / 16;  // QK MFMAs per 32-key block (64 or 16 features each)
     constexpr int DB = D / 32;    // 32-feature blocks of the O^T accumulator
-    constexpr int CPR = D / 8;    // 16-byte chunks per key row
-    constexpr int NCH = kBN * CPR / kGThreads;  // 16-byte chunks each thread stages per tile
+    constexpr int CPR = D / EPC;  // 16-byte chunks per key row (global memory)
+    constexpr int kChunks = kBN * CPR;
+    constexpr int NCH = kChunks >= kGThreads ? kChunks / kGThreads : 1;  // chunks per thread per tile
     constexpr int RSTEP = kGThreads / CPR;      // key rows between a thread's chunks
-    static_assert(NCH * kGThreads == kBN * CPR, "tile must split evenly over the key group");
+    static_assert(kChunks < kGThreads ? kGThreads % kChunks == 0 && kChunks % 64 == 0
+                                      : NCH * kGThreads == kChunks,
+                  "tile must split evenly over the key group (or over whole waves of it)");
     static_assert(KS == 1 || KS == 2, "one or two key groups");
 
     // Each key group owns two K slots and two V slots (double buffering) in LDS. K and V are
     // separate arrays so every LDS offset stays within the 16-bit immediate of ds_read/ds_write.
     constexpr int kKSlot = kBN * KST, kVSlot = kBN * VST;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KS][2 * kKSlot];
+    __shared__ __attribute__((aligned(16))) In Ks[KS][2 * kKSlot];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KS][2 * kVSlot];
 
     const int tid = threadIdx.x;
@@ -196,52 +232,78 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     }
     const unsigned key_span = (unsigned)(key_hi - key_lo);
 
-    // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row.
-    u32x4 qf[DC];
+    // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row (16-bit
+    // inputs), or [64c + 32g, 64c + 32g + 32) (FP8, two 16-byte loads per MFMA).
+    const In* const pq = static_cast<const In*>(p.q);
+    const In* const pk = static_cast<const In*>(p.k);
+    const In* const pv = static_cast<const In*>(p.v);
+    using QOp = std::conditional_t<FP8, i32x8, u32x4>;
+    QOp qf[DC];
     {
-        const uint16_t* qp = p.q + b * p.q_bstride + (int64_t)min(qrow, p.Lq - 1) * p.q_tstride + h * D + 8 * g;
+        const In* qp = pq + b * p.q_bstride + (int64_t)min(qrow, p.Lq - 1) * p.q_tstride + h * D + (FP8 ? 32 : 8) * g;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
+        for (int c = 0; c < DC; ++c) {
+            if constexpr (FP8) {
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(qp + 64 * c);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(qp + 64 * c + 16);
+                qf[c] = __builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}));
+            } else {
+                qf[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
+            }
+        }
     }
 
-    // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, features
-    // scol..scol+7) of every tile; rows past Lk re-read row Lk - 1 (their scores are masked).
+    // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, EPC input
+    // features from scol) of every tile; rows past Lk re-read row Lk - 1 (their scores are
+    // masked). When a tile has fewer chunks than the group has threads, whole waves sit out.
     const int tid_g = KS == 1 ? tid : tid % kGThreads;
-    const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * 8;
-    const uint16_t* kg = p.k + b * p.kv_bstride + hk * D + scol;
-    const uint16_t* vg = p.v + b * p.kv_bstride + hk * D + scol;
-    uint16_t* const Kg = &Ks[ks][0];  // this group's K and V slots
+    const bool stager = kChunks >= kGThreads || tid_g < kChunks;
+    const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * EPC;
+    const In* kg = pk + b * p.kv_bstride + hk * D + scol;
+    const In* vg = pv + b * p.kv_bstride + hk * D + scol;
+    In* const Kg = &Ks[ks][0];  // this group's K and V slots (V always f16 in LDS)
     uint16_t* const Vg = &Vs[ks][0];
-    uint16_t* ks_st = Kg + srow0 * KST + scol;
+    In* ks_st = Kg + srow0 * KST + scol;
     uint16_t* vs_st = Vg + srow0 * VST + scol;
     u32x4 kreg[NCH], vreg[NCH];
     auto load_k = [&](int kt) __attribute__((always_inline)) {
+        if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
             const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
             kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * p.kv_tstride);
         });
     };
     auto load_v = [&](int kt) __attribute__((always_inline)) {
+        if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
             const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
             vreg[u] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * p.kv_tstride);
         });
     };
     auto store_k = [&](int slot) __attribute__((always_inline)) {
+        if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
             *reinterpret_cast<u32x4*>(ks_st + slot * (kBN * KST) + u * RSTEP * KST) = kreg[u];
         });
     };
     auto store_v = [&](int slot) __attribute__((always_inline)) {
+        if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            *reinterpret_cast<u32x4*>(vs_st + slot * (kBN * VST) + u * RSTEP * VST) =
-                BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+            uint16_t* dst = vs_st + slot * (kBN * VST) + u * RSTEP * VST;
+            if constexpr (FP8) {
+                u32x4 lo, hi;
+                fp8x16_to_f16x16(vreg[u], lo, hi);
+                *reinterpret_cast<u32x4*>(dst) = lo;
+                *reinterpret_cast<u32x4*>(dst + 8) = hi;
+            } else {
+                *reinterpret_cast<u32x4*>(dst) = BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+            }
         });
     };
 
     // LDS read addresses (address space 3, so constant offsets fold into the instructions).
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
-    lds_u4* kq_lane = (lds_u4*)(Kg + j * KST + 8 * g);
+    lds_u4* kq_lane = (lds_u4*)(Kg + j * KST + (FP8 ? 32 : 8) * g);
     // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
     // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
     const int G = lane >> 4, L16 = lane & 15;
@@ -275,8 +337,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
-                for (int cc = 0; cc < DC; ++cc)
-                    sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
+                for (int cc = 0; cc < DC; ++cc) {
+                    if constexpr (FP8) {
+                        const int off = ((t & 1) * kBN * KST + kb * 32 * KST + 64 * cc) / 16;
+                        const u32x4 lo = kq_lane[off], hi = kq_lane[off + 1];
+                        sc[kb] = mfma_qk_fp8(__builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w})),
+                                             qf[cc], sc[kb]);
+                    } else {
+                        sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
+                    }
+                }
             }
         }
         if constexpr (PV) {
@@ -397,34 +467,44 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     if constexpr (KS == 2) {
         // Merge the two key groups' partial results through LDS (the tiles are no longer read:
         // every step ended with a barrier): (m, l, O) = (max, l0 a0 + l1 a1, O0 a0 + O1 a1) with
-        // a_i = exp2(m_i - m). Group 1 hands over -- the first half of O in the K buffers, the
-        // rest with m and l in the V buffers -- and group 0 merges and stores.
-        constexpr int NA = 16 * (DB / 2), NB = 16 * (DB - DB / 2) + 2;
-        static_assert(kRW * NA * 64 * 4 <= (int)sizeof(Ks) && kRW * NB * 64 * 4 <= (int)sizeof(Vs),
-                      "merge area must fit in the tile buffers");
-        float* mrg_a = reinterpret_cast<float*>(&Ks[0][0]) + rw * NA * 64 + lane;
-        float* mrg_b = reinterpret_cast<float*>(&Vs[0][0]) + rw * NB * 64 + lane;
-        auto slot = [&](int db, int r) __attribute__((always_inline)) -> float* {
-            return db < DB / 2 ? mrg_a + (16 * db + r) * 64 : mrg_b + (16 * (db - DB / 2) + r) * 64;
-        };
+        // a_i = exp2(m_i - m). Group 1 hands over m and l through the K buffers and O through
+        // the V buffers, DBR 32-feature blocks per round; group 0 merges and stores.
+        constexpr int kPerDb = kRW * 16 * 64;  // floats of one 32-feature block, all row waves
+        constexpr int DBR = (int)(sizeof(Vs) / 4 / kPerDb) < DB ? (int)(sizeof(Vs) / 4 / kPerDb) : DB;
+        static_assert(DBR >= 1 && kRW * 128 * 4 <= (int)sizeof(Ks), "merge areas must fit in the tile buffers");
+        float* ml = reinterpret_cast<float*>(&Ks[0][0]) + rw * 128 + lane;
+        float* area = reinterpret_cast<float*>(&Vs[0][0]) + rw * (DBR * 16 * 64) + lane;
         if (ks == 1) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) *slot(db, r) = o[db][r];
-            mrg_b[(NB - 2) * 64] = m_run;
-            mrg_b[(NB - 1) * 64] = l_run;
+            ml[0] = m_run;
+            ml[64] = l_run;
         }
         __syncthreads();
+        float a0 = 1.f, a1 = 0.f;
+        if (ks == 0) {
+            const float m1 = ml[0], l1 = ml[64];
+            const float mn = fmaxf(m_run, m1);
+            a0 = __builtin_amdgcn_exp2f(m_run - mn);
+            a1 = __builtin_amdgcn_exp2f(m1 - mn);
+            l_run = l_run * a0 + l1 * a1;
+        }
+#pragma unroll
+        for (int d0 = 0; d0 < DB; d0 += DBR) {
+            if (ks == 1) {
+#pragma unroll
+                for (int db = d0; db < d0 + DBR && db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) area[((db - d0) * 16 + r) * 64] = o[db][r];
+            }
+            __syncthreads();
+            if (ks == 0) {
+#pragma unroll
+                for (int db = d0; db < d0 + DBR && db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + area[((db - d0) * 16 + r) * 64] * a1;
+            }
+            if (d0 + DBR < DB) __syncthreads();  // the next round overwrites the area
+        }
         if (ks == 1) return;
-        const float m1 = mrg_b[(NB - 2) * 64], l1 = mrg_b[(NB - 1) * 64];
-        const float mn = fmaxf(m_run, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + *slot(db, r) * a1;
-        l_run = l_run * a0 + l1 * a1;
     }
 
     // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
@@ -440,7 +520,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
                 const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
                 u32x2 w;
-                if constexpr (BF16) {
+                if constexpr (OUT_BF16) {
                     w.x = pack_bf16x2(x0, x1);
                     w.y = pack_bf16x2(x2, x3);
                 } else {
@@ -466,13 +546,13 @@ int device_cu_count() {
     return cached_cus;
 }
 
-template <int D, bool BF16, int NW, int KS>
+template <int D, int DT, int NW, int KS>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     constexpr int kBM = NW / KS * 32;
     KParams p;
-    p.q = static_cast<const uint16_t*>(a.q);
-    p.k = static_cast<const uint16_t*>(a.k);
-    p.v = static_cast<const uint16_t*>(a.v);
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
     p.out = static_cast<uint16_t*>(a.out);
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;
@@ -489,11 +569,11 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     p.c = a.scale * kLog2e;
     const int64_t nblocks = (int64_t)p.n_qblk * a.Hq * a.B;
     p.nblocks = (int)nblocks;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, NW, KS>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, int DT>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // 256-row workgroups when there are at least four per CU (long sequences). Otherwise 128-row
     // workgroups of 4 waves, two per CU -- unless even those leave CUs with a single 4-wave
@@ -504,18 +584,21 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // balancing gains) nor for loops of a few tiles (the merge does not amortise).
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
-    if (wg256 >= 4 * cus) return launch<D, BF16, 8, 1>(a, stream);
+    if (wg256 >= 4 * cus) return launch<D, DT, 8, 1>(a, stream);
     const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
-    if (wg128 <= cus && a.Lk >= 512) return launch<D, BF16, 8, 2>(a, stream);
-    return launch<D, BF16, 4, 1>(a, stream);
+    if (wg128 <= cus && a.Lk >= 512) return launch<D, DT, 8, 2>(a, stream);
+    return launch<D, DT, 4, 1>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
-    const bool bf16 = a.dtype == 0;
-    if (a.d == 128) return bf16 ? launch_shape<128, true>(a, stream) : launch_shape<128, false>(a, stream);
-    return bf16 ? launch_shape<64, true>(a, stream) : launch_shape<64, false>(a, stream);
+    if (a.d == 128) {
+        if (a.dtype == kDtFP8) return launch_shape<128, kDtFP8>(a, stream);
+        return a.dtype == kDtBF16 ? launch_shape<128, kDtBF16>(a, stream) : launch_shape<128, kDtF16>(a, stream);
+    }
+    if (a.dtype == kDtFP8) return launch_shape<64, kDtFP8>(a, stream);
+    return a.dtype == kDtBF16 ? launch_shape<64, kDtBF16>(a, stream) : launch_shape<64, kDtF16>(a, stream);
 }
 
 }  // namespace sa

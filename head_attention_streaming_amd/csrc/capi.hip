@@ -48,8 +48,8 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lq < 0 || Lk < 0)
         return fail(SA_ERR_RANGE, "attn_forward: negative or zero size (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d)", B, Hq,
                     Hkv, Lq, Lk);
-    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16)
-        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0) or f16 (1)", dtype);
+    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16 && dtype != SA_DTYPE_FP8_E4M3)
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0), f16 (1) or fp8 e4m3 (2)", dtype);
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward: head dim %d not built (64, 128)", d);
     if (Hq % Hkv != 0) return fail(SA_ERR_SHAPE, "attn_forward: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (win_left < -1 || win_right < -1)
@@ -71,7 +71,9 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
         return fail(SA_ERR_RANGE, "attn_forward: tensor too large");
     if (kv_bstride < nkv) return fail(SA_ERR_SHAPE, "attn_forward: kv_bstride %lld < Lk*Hkv*d %lld",
                                       (long long)kv_bstride, (long long)nkv);
-    if (kv_bstride % 8) return fail(SA_ERR_ALIGN, "attn_forward: kv_bstride must be a multiple of 8 elements");
+    const int elem_bytes = dtype == SA_DTYPE_FP8_E4M3 ? 1 : 2;
+    if ((kv_bstride * elem_bytes) % 16)
+        return fail(SA_ERR_ALIGN, "attn_forward: kv_bstride must be a multiple of 16 bytes");
     if (mul4(B, kv_bstride, 1, 1) < 0) return fail(SA_ERR_RANGE, "attn_forward: K/V extent overflows");
     const int64_t nblocks = (int64_t)((Lq + 127) / 128) * Hq * B;
     if (nblocks > INT32_MAX) return fail(SA_ERR_RANGE, "attn_forward: grid too large");

@@ -106,6 +106,15 @@ WORKLOADS = {
     # long non-causal MHA, [1, 20480, 56, 128] bf16
     "mha_20480_bf16": Workload("mha_20480_bf16", 1, 56, 56, 20480, 20480, 128, "bf16", False,
                                128 ** -0.5, 1005),
+    # 32 query heads over 32, 8 or 1 K/V heads: what re-reading a shared K/V head costs
+    "mha_8192_h32_bf16": Workload("mha_8192_h32_bf16", 1, 32, 32, 8192, 8192, 128, "bf16", False, 128 ** -0.5, 1007),
+    "gqa_8192_h32kv8_bf16": Workload("gqa_8192_h32kv8_bf16", 1, 32, 8, 8192, 8192, 128, "bf16", False,
+                                     128 ** -0.5, 1007),
+    "mqa_8192_h32kv1_bf16": Workload("mqa_8192_h32kv1_bf16", 1, 32, 1, 8192, 8192, 128, "bf16", False,
+                                     128 ** -0.5, 1007),
+    # the long problem with unscaled FP8 E4M3 q, k, v (bf16 out)
+    "mha_20480_fp8": Workload("mha_20480_fp8", 1, 56, 56, 20480, 20480, 128, "e4m3", False,
+                              128 ** -0.5, 1005),
     # sliding-window (local) attention, [4, 4096, 32, 64] fp16, 256 keys back + the query's own
     "window_4096_w256_f16": Workload("window_4096_w256_f16", 4, 32, 32, 4096, 4096, 64, "f16", False,
                                      0.125, 1006, attn_window=(256, 0)),

@@ -44,7 +44,10 @@ typedef enum {
     SA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 } sa_status;
 
-enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1 };
+/* Element types. SA_DTYPE_FP8_E4M3 (attention inputs only): OCP FP8 E4M3, the unscaled
+ * float8_e4m3fn of the quantized-SDPA option (page "flashdreams.accelerated", section
+ * OptimizedMultiHeadAttention); q, k and v are one byte per element, out is bf16. */
+enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1, SA_DTYPE_FP8_E4M3 = 2 };
 
 /* Q/K normalisation scope: none, per head (m = d), or inner (m = H*d: all heads of a token). */
 enum { SA_NORM_NONE = 0, SA_NORM_HEAD = 1, SA_NORM_INNER = 2 };
@@ -193,8 +196,11 @@ int attn_forward_f16(const void* q, const void* k, const void* v, void* out,
  * attn_forward_kvstride -- attention over the first Lk tokens of a larger K/V buffer, such as
  * a rolling cache [B, S, Hkv, d] with S >= Lk (streaming self-attention) or a static context
  * cache (cross-attention). kv_bstride is the element distance between batches of k and v
- * (S*Hkv*d for a cache; >= Lk*Hkv*d). dtype is SA_DTYPE_BF16 or SA_DTYPE_F16 for all four
- * tensors. Otherwise identical to attn_forward.
+ * (S*Hkv*d for a cache; >= Lk*Hkv*d; a multiple of 16 bytes). dtype is SA_DTYPE_BF16 or
+ * SA_DTYPE_F16 for all four tensors, or SA_DTYPE_FP8_E4M3 for q, k and v with a bf16 out.
+ * FP8: Q K^T runs on the FP8 MFMA with fp32 accumulation from the exact E4M3 values; V is
+ * widened exactly to f16 and P V is computed as for 16-bit inputs (f16 probabilities), so the
+ * only FP8 rounding is the caller's cast of Q, K and V. Otherwise identical to attn_forward.
  */
 int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out,
                           int B, int Hq, int Hkv, int Lq, int Lk, int d,
@@ -212,7 +218,8 @@ int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out
  *   window_left, window_right  >= -1. With window_right >= 0, Lq <= Lk + window_right is
  *            required so that every query sees at least one key (SA_ERR_SHAPE otherwise).
  * Key tiles that lie outside every query's band of a workgroup are skipped, so the work is
- * proportional to the keys in the band. Everything else as attn_forward_kvstride.
+ * proportional to the keys in the band. Everything else (dtypes included) as
+ * attn_forward_kvstride.
  */
 int attn_forward_window(const void* q, const void* k, const void* v, void* out,
                         int B, int Hq, int Hkv, int Lq, int Lk, int d,

@@ -172,3 +172,11 @@ def test_kv_cache_rope_rejects_bad_arguments():
     assert L.kv_cache_rope(P, Q, P, 1, 0, 128, 16, 0, 64, 0, 1, None) == -5      # no heads
     out = (ctypes.c_int64 * 4)()
     assert L.kv_cache_positions(5, 16, 0, 64, out, 4) == -5                      # output too small
+
+
+def test_fp8_kv_stride_must_be_16_bytes():
+    L = lib()
+    P = ctypes.c_void_p(4096)
+    # 100*4*64 + 8 elements is 16-byte aligned for 16-bit types but not for one-byte FP8
+    assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 100 * 4 * 64 + 8, 2, None) == -4
+    assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 100 * 4 * 64, 3, None) == -3
