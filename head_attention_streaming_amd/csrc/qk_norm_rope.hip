@@ -71,7 +71,9 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
     return u32x4{a[0], a[1], a[2], a[3]};
 }
 
-template <int D>
+// NORM: the norm scope (0 none, 1 head, 2 inner) as a template parameter, so the head-scope
+// kernel carries no inner-scope state and keeps three workgroups per CU.
+template <int D, int NORM>
 __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs a) {
     constexpr int LPR = D / 8;            // lanes per head row
     constexpr int RPP = kThreads / LPR;   // head rows per pass
@@ -141,7 +143,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     // features), so the sums of squares are reduced over the workgroup before any row is
     // normalised. The first batch of rows is already in registers; later batches are read twice.
     float r_q = 1.f, r_k = 1.f;
-    if (a.norm_scope == 2) {
+    if constexpr (NORM == 2) {
         float sq = 0.f, sk = 0.f;
         for (int base = 0; base < rows_padded; base += NB * RPP) {
             if (base > 0) load_batch(base);
@@ -182,7 +184,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     float gq[8], gk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) gq[e] = gk[e] = 1.f;
-    if (a.norm_scope == 1) {  // uniform: two 16-byte loads per weight vector
+    if constexpr (NORM == 1) {  // uniform: two 16-byte loads per weight vector
         const f32x4* pq = reinterpret_cast<const f32x4*>(a.gamma_q + f0);
         const f32x4 q0 = pq[0], q1 = pq[1];
 #pragma unroll
@@ -210,7 +212,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
             const bool is_q = row < a.Hq;
             float z[8];
             unpack_bf16x8(raw[nb], z);
-            if (a.norm_scope == 1) {
+            if constexpr (NORM == 1) {
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
                 const float r = 1.f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
-            } else if (a.norm_scope == 2 && valid) {
+            } else if (NORM == 2 && valid) {
                 // weights of this row's features: gamma[h*d + f0 .. + 8]
                 const f32x4* pg = reinterpret_cast<const f32x4*>(
                     is_q ? a.gamma_q + row * D + f0 : a.gamma_k + (row - a.Hq) * D + f0);
@@ -261,12 +263,22 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
 
 }  // namespace
 
+template <int D>
+void launch_d(const NormRopeArgs& a, dim3 grid, hipStream_t stream) {
+    if (a.norm_scope == 1)
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.norm_scope == 2)
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 0>), grid, dim3(kThreads), 0, stream, a);
+}
+
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.L));
     if (a.d == 128)
-        hipLaunchKernelGGL(qk_norm_rope_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+        launch_d<128>(a, grid, stream);
     else
-        hipLaunchKernelGGL(qk_norm_rope_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+        launch_d<64>(a, grid, stream);
     return hipGetLastError();
 }
 
