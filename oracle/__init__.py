@@ -109,11 +109,12 @@ _FORMATS = {
     # significant bits (including the implicit one), smallest normal exponent, largest finite value
     "bf16": (8, -126, (2.0 - 2.0 ** -7) * 2.0 ** 127),
     "f16": (11, -14, 65504.0),
+    "e4m3": (4, -6, 448.0),   # OCP FP8 E4M3 (float8_e4m3fn): no infinity, overflow is NaN
 }
 
 
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to the nearest ``dtype`` value, ties to even, in one step.
+    """Round float64 values to the nearest ``dtype`` value ("bf16", "f16", "e4m3"), ties to even, in one step.
 
     A value with binary exponent e (x = f * 2^e, 0.5 <= |f| < 1) has quantum
     2^(e - p) for a p-bit significand, floored at the subnormal quantum 2^(emin - p + 1).
@@ -126,6 +127,11 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
     q_exp = np.maximum(e - p, emin - p + 1)
     q = np.ldexp(np.ones_like(x), q_exp)
     r = np.rint(x / q) * q
+    if dtype == "e4m3":
+        # E4M3 has no infinity: a result beyond 448 after rounding (|x| > 464; 464 itself is a tie
+        # that rounds to the even 448) is NaN, as is a NaN input
+        r = np.where(np.abs(r) > fmax, np.nan, r)
+        return np.where(x == 0, x, r)
     # overflow: anything at or beyond the midpoint between fmax and the next (virtual) step
     top = fmax + 0.5 * np.ldexp(1.0, int(np.frexp(fmax)[1]) - p)
     r = np.where(np.abs(x) >= top, np.copysign(np.inf, x), r)

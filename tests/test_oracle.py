@@ -425,3 +425,27 @@ def test_after_cache_positions_close_the_gap_after_a_sink():
     positions, far from it in absolute ones: the two readings must differ."""
     before, after = _after_vs_before(Lc=4, sink=4, window=8, n_chunks=6)
     assert np.abs(after - before).max() > 1e-3
+
+
+def test_round_to_e4m3_matches_the_format_and_torch():
+    """RNE into OCP E4M3 (float8_e4m3fn): hand cases from the format (3 fraction bits, subnormal
+    quantum 2^-9, largest 448, no infinity) and torch's float8_e4m3fn cast on many values."""
+    hand = {1.0625: 1.0, 1.1875: 1.25, 1.0625 + 2 ** -20: 1.125, 2.0 ** -10: 0.0, 3 * 2.0 ** -11: 2.0 ** -9,
+            448.0: 448.0, 464.0: 448.0, 300.0: 288.0, -0.3: -0.3125, 2.0 ** -9: 2.0 ** -9, 0.0: 0.0}
+    for x, want in hand.items():
+        assert oracle.round_to(np.array([x]), "e4m3")[0] == want, x
+    assert np.isnan(oracle.round_to(np.array([464.5, -500.0, 1e9]), "e4m3")).all()
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 200.0)])
+    codes = oracle.decode(np.arange(256, dtype=np.uint8), "e4m3")
+    codes = codes[np.isfinite(codes)]
+    mids = (np.sort(codes)[1:] + np.sort(codes)[:-1]) / 2      # exact ties between neighbours
+    # float32 inputs (torch casts through float32, so a float64 input one step off a tie would be
+    # rounded twice there); the neighbours of each tie are float32 neighbours
+    m32 = mids.astype(np.float32)
+    vals = np.concatenate([vals.astype(np.float32), codes.astype(np.float32), m32,
+                           np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(-np.inf))])
+    vals = vals[np.abs(vals) <= 464.0]
+    ours = oracle.round_to(vals.astype(np.float64), "e4m3")
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
