@@ -127,7 +127,8 @@ def make_workload(name: str, dev: str):
     # streaming self-attention: steady state (cache full, every step evicts the oldest chunk)
     Lc, S = w.chunk, w.window
     after = w.rope_scope == "after"
-    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, device=dev, after_cache_rope=after)
+    cdt = synthetic.DTYPES[w.cache_dtype]
+    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, dtype=cdt, device=dev, after_cache_rope=after)
     g = torch.Generator().manual_seed(w.seed)
     gq, gk = synthetic.norm_weight(w.d, g).to(dev), synthetic.norm_weight(w.d, g).to(dev)
     nsets = 6  # rotate input sets (6 x 55 MB) so the prologue and append are not served from cache
@@ -135,8 +136,8 @@ def make_workload(name: str, dev: str):
     for i in range(nsets):
         gi = torch.Generator().manual_seed(w.seed + i)
         sets.append([synthetic.normal((w.B, Lc, w.Hq, w.d), "bf16", gi).to(dev) for _ in range(3)])
-    q_buf = torch.empty((w.B, Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
-    out = torch.empty_like(q_buf)
+    q_buf = torch.empty((w.B, Lc, w.Hq, w.d), dtype=cdt, device=dev)
+    out = torch.empty((w.B, Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
     state = {"c": 0}
     if after:  # rows 0 .. visible-1 of the visible sequence (visible = S once the cache is full)
         vis_angles = synthetic.rope_angles(np.arange(S), w.d).to(dev)
@@ -178,11 +179,14 @@ def make_workload(name: str, dev: str):
         binding.kv_cache_append(None, v, None, cache.v, state["c"], 0, S)
 
     elem = 2 * w.B * Lc * w.Hq * w.d  # bytes of one [B, Lc, H, d] bf16 tensor
+    out_elem = elem // 2 if w.cache_dtype == "e4m3" else elem   # the same tensor in the cache type
+    info["cache_dtype"] = w.cache_dtype
     info["hbm_steps"] = {
-        "qk_norm_rope": (prologue, 4 * elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4),  # q,k read + written, angles, gammas
+        # q, k read (bf16) + written (cache type), angles, gammas
+        "qk_norm_rope": (prologue, 2 * elem + 2 * out_elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4),
         "qk_norm_rope_inner": (lambda: prologue(binding.SA_NORM_INNER),
-                               4 * elem + Lc * (w.d // 2) * 4 + 2 * w.Hq * w.d * 4),  # inner-scope weights
-        "kv_cache_append": (append, 2 * elem),                                   # v read + written
+                               2 * elem + 2 * out_elem + Lc * (w.d // 2) * 4 + 2 * w.Hq * w.d * 4),
+        "kv_cache_append": (append, elem + out_elem),                            # v read + written
     }
     if after:
         def cache_rope():
@@ -309,7 +313,8 @@ def main():
         info["hbm_kernels"] = hbm
 
     flops = workload_flops(w)
-    peak = PEAK_MFMA_FP8_F16 if w.dtype == "e4m3" else PEAK_MFMA_16BIT
+    fp8 = w.dtype == "e4m3" or w.cache_dtype == "e4m3"
+    peak = PEAK_MFMA_FP8_F16 if fp8 else PEAK_MFMA_16BIT
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kern * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
@@ -324,13 +329,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "e4m3" if fp8 else w.dtype,
         "data": "synthetic",
         "config": dict(info, flops_per_step=flops, pct_of_bf16_peak=round(100 * value / PEAK_MFMA_16BIT, 2),
                        wall_ms_per_step=round(wall_ms, 4)),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"attn_fwd_kernel<{w.d},{w.dtype}>",
+                     "kernel": f"attn_fwd_kernel<{w.d},{'e4m3' if fp8 else w.dtype}>",
                      "kernel_ms": round(ms_kern, 4)},
         "cpu_baseline": None,
     }

@@ -15,11 +15,13 @@ import torch
 from . import build as _build
 
 SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3 = 0, 1, 2
+SA_ERR_UNSUPPORTED_CODE = -3
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
 
-EXPORTS = ("qk_norm_rope", "kv_cache_slot", "kv_cache_positions", "kv_cache_append", "kv_cache_rope",
-           "attn_forward", "attn_forward_f16", "attn_forward_kvstride", "attn_forward_window", "sa_last_error")
+EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
+           "kv_cache_append_ex", "kv_cache_rope", "attn_forward", "attn_forward_f16", "attn_forward_kvstride",
+           "attn_forward_window", "sa_last_error")
 
 _lib = None
 
@@ -46,6 +48,8 @@ def lib():
         L.qk_norm_rope.argtypes = [P, P, I64, P, P, I64, P, P, P, I, I, I, I, I, F, I, I, P]
         L.kv_cache_slot.argtypes = [I64, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I)]
         L.kv_cache_append.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, P]
+        L.kv_cache_append_ex.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I, I, P]
+        L.qk_norm_rope_ex.argtypes = [P, P, I64, P, P, I64, P, P, P, I, I, I, I, I, F, I, I, I, P]
         L.kv_cache_positions.argtypes = [I64, I, I, I, ctypes.POINTER(I64), I]
         L.kv_cache_rope.argtypes = [P, P, P, I, I, I, I, I, I, I64, I, P]
         L.attn_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
@@ -136,7 +140,8 @@ def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk:
 def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None, angles=None, eps: float = 1e-6,
                  norm_scope: int = SA_NORM_HEAD, rope_style: int = SA_ROPE_SPLIT, q_out_bstride=None,
                  k_out_bstride=None, Hkv: int | None = None):
-    """RMSNorm (head or inner scope) then RoPE of q_in (and k_in) into q_out (and k_out), bf16.
+    """RMSNorm (head or inner scope) then RoPE of q_in (and k_in) into q_out (and k_out); bf16 in,
+    bf16 or float8_e4m3fn out (the type of q_out; k_out must have the same type).
 
     q_in [B, L, Hq, d]; k_out may be a view of a cache row range (pass k_out_bstride = S*Hkv*d).
     rope_style | SA_ROPE_AFTER_CACHE rotates the queries only (keys are normalised, unrotated).
@@ -148,9 +153,11 @@ def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None,
         q_out_bstride = L * Hq * d
     if k_out_bstride is None:
         k_out_bstride = L * Hkv * d
-    _check("qk_norm_rope", lib().qk_norm_rope(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
-                                              k_out_bstride, _ptr(gamma_q), _ptr(gamma_k), _ptr(angles), B, L, Hq,
-                                              Hkv, d, float(eps), norm_scope, rope_style, _stream(q_in)))
+    out_dtype = _dtype_code(q_out)
+    _check("qk_norm_rope_ex", lib().qk_norm_rope_ex(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
+                                                    k_out_bstride, _ptr(gamma_q), _ptr(gamma_k), _ptr(angles), B, L,
+                                                    Hq, Hkv, d, float(eps), norm_scope, rope_style, out_dtype,
+                                                    _stream(q_in)))
 
 
 def kv_cache_slot(chunk_idx: int, chunk_len: int, sink_size: int, window_size: int):
@@ -182,11 +189,19 @@ def kv_cache_rope(cache_k, k_rot, angles, chunk_idx: int, chunk_len: int, sink_s
 
 
 def kv_cache_append(k_new, v_new, cache_k, cache_v, chunk_idx: int, sink_size: int, window_size: int):
-    """Copy k_new / v_new [B, Lc, Hkv, d] (either may be None) into their cache slot range."""
+    """Copy k_new / v_new [B, Lc, Hkv, d] (either may be None) into their cache slot range; a cache of
+    another element type (float8_e4m3fn or f16 for bf16 input) receives the rounded values."""
     ref = v_new if v_new is not None else k_new
+    dst = cache_v if v_new is not None else cache_k
     B, Lc, Hkv, d = ref.shape
-    _check("kv_cache_append", lib().kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B, Lc,
-                                                    Hkv, d, sink_size, window_size, int(chunk_idx), _stream(ref)))
+    if ref.dtype == dst.dtype and ref.element_size() == 2:  # any 16-bit type: a byte copy
+        _check("kv_cache_append", lib().kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B,
+                                                        Lc, Hkv, d, sink_size, window_size, int(chunk_idx),
+                                                        _stream(ref)))
+        return
+    _check("kv_cache_append_ex", lib().kv_cache_append_ex(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B,
+                                                          Lc, Hkv, d, sink_size, window_size, int(chunk_idx),
+                                                          _dtype_code(ref), _dtype_code(dst), _stream(ref)))
 
 
 class BlockKVCache:
@@ -236,6 +251,9 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
                                rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD):
     """One streaming self-attention chunk as library calls between before_update / after_update.
 
+    A cache of float8_e4m3fn (BlockKVCache(dtype=torch.float8_e4m3fn), before-cache RoPE only) with
+    an E4M3 q_buf is the FP8 path: the prologue rounds Q and K to E4M3, the append rounds V, and
+    attention runs on the FP8 MFMA with a bf16 out.
     Before-cache RoPE (cache.k_rot is None): angles [Lc, d/2] for the chunk's positions;
     qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot, both rotated) ->
     kv_cache_append (v_in -> cache values) -> attn_forward_kvstride over the visible cache.
@@ -248,6 +266,9 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
     after = cache.k_rot is not None
+    if after and cache.k.dtype != torch.bfloat16:
+        raise StreamAttnError("stream_self_attention_step", SA_ERR_UNSUPPORTED_CODE,
+                              "after-cache RoPE is built for a bf16 cache only")
     q_angles = angles[visible - cache.chunk_len:visible] if after else angles
     qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
                  norm_scope, rope_style | (SA_ROPE_AFTER_CACHE if after else 0),

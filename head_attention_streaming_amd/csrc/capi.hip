@@ -165,14 +165,23 @@ int kv_cache_slot(int64_t chunk_idx, int chunk_len, int sink_size, int window_si
     return ok();
 }
 
-int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* cache_v, int B, int Lc, int Hkv,
-                    int d, int sink_size, int window_size, int64_t chunk_idx, void* stream) {
+int kv_cache_append_ex(const void* k_new, const void* v_new, void* cache_k, void* cache_v, int B, int Lc, int Hkv,
+                       int d, int sink_size, int window_size, int64_t chunk_idx, int src_dtype, int cache_dtype,
+                       void* stream) {
     int64_t slot = 0;
     int vis = 0;
     const int st = kv_cache_slot(chunk_idx, Lc, sink_size, window_size, &slot, &vis);
     if (st != SA_OK) return st;
     if (B < 0 || Hkv <= 0) return fail(SA_ERR_RANGE, "kv_cache_append: B >= 0 and Hkv > 0 required");
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "kv_cache_append: head dim %d not built (64, 128)", d);
+    int cvt = -1;
+    if (src_dtype == cache_dtype && (src_dtype == SA_DTYPE_BF16 || src_dtype == SA_DTYPE_F16)) cvt = 0;
+    else if (src_dtype == SA_DTYPE_FP8_E4M3 && cache_dtype == SA_DTYPE_FP8_E4M3) cvt = 3;
+    else if (src_dtype == SA_DTYPE_BF16 && cache_dtype == SA_DTYPE_FP8_E4M3) cvt = 1;
+    else if (src_dtype == SA_DTYPE_BF16 && cache_dtype == SA_DTYPE_F16) cvt = 2;
+    if (cvt < 0)
+        return fail(SA_ERR_UNSUPPORTED, "kv_cache_append: no conversion from dtype %d to cache dtype %d", src_dtype,
+                    cache_dtype);
     if (!k_new && !v_new) return fail(SA_ERR_NULL, "kv_cache_append: both k_new and v_new are NULL");
     if ((k_new && !cache_k) || (v_new && !cache_v)) return fail(SA_ERR_NULL, "kv_cache_append: null cache pointer");
     for (const void* p : {k_new, v_new, (const void*)cache_k, (const void*)cache_v})
@@ -188,22 +197,33 @@ int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* c
         const void* src = which ? v_new : k_new;
         void* dst = which ? cache_v : cache_k;
         if (!src) continue;
-        sa::CopyArgs c;
+        sa::CopyArgs c{};
         c.src = src;
         c.dst = dst;
         c.B = B;
         c.row_elems = chunk_elems;
         c.dst_bstride = cap * row;
         c.dst_offset = slot * row;
+        c.cvt = cvt;
         const int s = hip_status(sa::launch_copy_rows(c, static_cast<hipStream_t>(stream)), "kv_cache_append launch");
         if (s != SA_OK) return s;
     }
     return ok();
 }
 
-int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
-                 int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
-                 int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, void* stream) {
+int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* cache_v, int B, int Lc, int Hkv,
+                    int d, int sink_size, int window_size, int64_t chunk_idx, void* stream) {
+    // a 16-bit byte copy: bf16 and f16 move alike
+    return kv_cache_append_ex(k_new, v_new, cache_k, cache_v, B, Lc, Hkv, d, sink_size, window_size, chunk_idx,
+                              SA_DTYPE_BF16, SA_DTYPE_BF16, stream);
+}
+
+int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
+                    int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
+                    int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, int out_dtype,
+                    void* stream) {
+    if (out_dtype != SA_DTYPE_BF16 && out_dtype != SA_DTYPE_FP8_E4M3)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: output dtype %d is not bf16 (0) or fp8 e4m3 (2)", out_dtype);
     if (B < 0 || L < 0 || Hq <= 0 || (k_in && Hkv <= 0))
         return fail(SA_ERR_RANGE, "qk_norm_rope: negative or zero size");
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: head dim %d not built (64, 128)", d);
@@ -230,8 +250,9 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
         if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "qk_norm_rope: pointers must be 16-byte aligned");
     const int64_t nq = mul4(1, L, Hq, d);
     if (nq < 0 || mul4(B, L, k_in ? Hkv : 1, d) < 0) return fail(SA_ERR_RANGE, "qk_norm_rope: tensor too large");
-    if (q_out_bstride < nq || q_out_bstride % 8) return fail(SA_ERR_SHAPE, "qk_norm_rope: bad q_out_bstride");
-    if (k_in && (k_out_bstride < (int64_t)L * Hkv * d || k_out_bstride % 8))
+    const int align_elems = out_dtype == SA_DTYPE_FP8_E4M3 ? 16 : 8;  // 16-byte aligned batch strides
+    if (q_out_bstride < nq || q_out_bstride % align_elems) return fail(SA_ERR_SHAPE, "qk_norm_rope: bad q_out_bstride");
+    if (k_in && (k_out_bstride < (int64_t)L * Hkv * d || k_out_bstride % align_elems))
         return fail(SA_ERR_SHAPE, "qk_norm_rope: bad k_out_bstride");
     if ((int64_t)B * L > INT32_MAX) return fail(SA_ERR_RANGE, "qk_norm_rope: grid too large");
     sa::NormRopeArgs a{};
@@ -254,7 +275,15 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const voi
     a.norm_scope = norm_scope;
     a.rope_style = pairing;
     a.rope_keys = (rope_style & SA_ROPE_AFTER_CACHE) ? 0 : 1;
+    a.out_fp8 = out_dtype == SA_DTYPE_FP8_E4M3;
     return hip_status(sa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "qk_norm_rope launch");
+}
+
+int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
+                 int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
+                 int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, void* stream) {
+    return qk_norm_rope_ex(q_in, q_out, q_out_bstride, k_in, k_out, k_out_bstride, gamma_q, gamma_k, rope_angles, B,
+                           L, Hq, Hkv, d, eps, norm_scope, rope_style, SA_DTYPE_BF16, stream);
 }
 
 int kv_cache_positions(int64_t chunk_idx, int chunk_len, int sink_size, int window_size, int64_t* logical_rows_out,

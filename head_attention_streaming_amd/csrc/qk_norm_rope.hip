@@ -10,6 +10,8 @@
 // (in LDS) and reused by every head. A head row of d features is spread over d/8 lanes holding 8
 // features (one 16-byte load/store) each; the RMS reduction and the split-half partner exchange
 // are lane shuffles inside that group.
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -47,6 +49,7 @@ __device__ __forceinline__ float split_partner(float x) {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void unpack_bf16x8(u32x4 w, float* f) {
@@ -71,10 +74,22 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
     return u32x4{a[0], a[1], a[2], a[3]};
 }
 
+// 8 floats -> 8 OCP FP8 E4M3 bytes, round to nearest even; beyond 448 after rounding gives NaN
+// (the unscaled float8_e4m3fn cast)
+__device__ __forceinline__ u32x2_t pack_e4m3x8(const float* f) {
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+    return u32x2_t{(uint32_t)w0, (uint32_t)w1};
+}
+
 // NORM: the norm scope (0 none, 1 head, 2 inner) as a template parameter, so the head-scope
-// kernel carries no inner-scope state and keeps three workgroups per CU.
-template <int D, int NORM>
+// kernel carries no inner-scope state and keeps three workgroups per CU. OUT8: outputs are FP8
+// E4M3 (one byte per element) instead of bf16.
+template <int D, int NORM, bool OUT8>
 __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs a) {
+    using Out = std::conditional_t<OUT8, uint8_t, uint16_t>;
     constexpr int LPR = D / 8;            // lanes per head row
     constexpr int RPP = kThreads / LPR;   // head rows per pass
     constexpr int HALF = D / 2;
@@ -90,8 +105,8 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
     const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + b * a.q_in_bstride + (int64_t)p * a.Hq * D;
     const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
-    uint16_t* qout = static_cast<uint16_t*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
-    uint16_t* kout = a.k_out ? static_cast<uint16_t*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
+    Out* qout = static_cast<Out*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
+    Out* kout = a.k_out ? static_cast<Out*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
 
     // Rows are handled NB passes at a time: all NB loads are issued before any is used, so each
     // thread keeps NB 16-byte reads in flight. rows_padded keeps every lane of a row group in
@@ -253,8 +268,11 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
                 for (int e = 0; e < 8; ++e) o[e] = z[e];
             }
             if (valid) {
-                uint16_t* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
-                *reinterpret_cast<u32x4*>(dst + f0) = pack_bf16x8(o);
+                Out* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
+                if constexpr (OUT8)
+                    *reinterpret_cast<u32x2_t*>(dst + f0) = pack_e4m3x8(o);
+                else
+                    *reinterpret_cast<u32x4*>(dst + f0) = pack_bf16x8(o);
             }
         }
         if (base + NB * RPP < rows_padded) load_batch(base + NB * RPP);
@@ -263,22 +281,25 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
 
 }  // namespace
 
-template <int D>
+template <int D, bool OUT8>
 void launch_d(const NormRopeArgs& a, dim3 grid, hipStream_t stream) {
     if (a.norm_scope == 1)
-        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 1, OUT8>), grid, dim3(kThreads), 0, stream, a);
     else if (a.norm_scope == 2)
-        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 2, OUT8>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 0>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((qk_norm_rope_kernel<D, 0, OUT8>), grid, dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.L));
-    if (a.d == 128)
-        launch_d<128>(a, grid, stream);
-    else
-        launch_d<64>(a, grid, stream);
+    if (a.d == 128) {
+        if (a.out_fp8) launch_d<128, true>(a, grid, stream);
+        else launch_d<128, false>(a, grid, stream);
+    } else {
+        if (a.out_fp8) launch_d<64, true>(a, grid, stream);
+        else launch_d<64, false>(a, grid, stream);
+    }
     return hipGetLastError();
 }
 

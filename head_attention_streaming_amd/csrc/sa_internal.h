@@ -36,6 +36,7 @@ struct NormRopeArgs {
     int norm_scope;         // 0 none, 1 head, 2 inner
     int rope_style;         // 0 none, 1 split, 2 interleaved
     int rope_keys;          // rotate the k rows too (0: keys are normalised only)
+    int out_fp8;            // outputs are OCP FP8 E4M3 (1 byte) instead of bf16; strides in elements
     int ring_lc, ring_nsink, ring_nwin;  // ring_lc > 0: token p is physical row p of a rolling
     int64_t ring_chunk;                  // cache after chunk ring_chunk was written
 };
@@ -60,6 +61,7 @@ struct CopyArgs {
     int64_t row_elems;   // elements per (batch) block to copy = Lc*Hkv*d
     int64_t dst_bstride; // elements between batches of dst
     int64_t dst_offset;  // element offset of the first destination row in each batch
+    int cvt;             // 0: same-type 16-bit copy, 1: bf16 -> FP8 E4M3, 2: bf16 -> f16, 3: FP8 byte copy
 };
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);

@@ -82,6 +82,7 @@ class Workload:
     window: int = 0          # streaming: cache capacity in tokens (sink 0)
     attn_window: tuple | None = None  # local attention band (left, right) around i + Lk - Lq
     rope_scope: str = "before"        # streaming: RoPE before or after the K/V cache update
+    cache_dtype: str = "bf16"         # streaming: element type of the K/V cache and attention inputs
 
     @property
     def flops(self) -> float:
@@ -100,6 +101,9 @@ WORKLOADS = {
     # the same streaming step with after-cache RoPE: unrotated cache, visible keys rotated per step
     "stream_after_1785x4": Workload("stream_after_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
                                     128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, rope_scope="after"),
+    # the same streaming step with an FP8 E4M3 K/V cache (Q, K, V rounded to E4M3, bf16 out)
+    "stream_fp8_1785x4": Workload("stream_fp8_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
+                                  128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, cache_dtype="e4m3"),
     # cross-attention over a static 512-token context, B = 2 (guidance pair), Q RMSNorm only
     "cross_1785x512": Workload("cross_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
                                128 ** -0.5, 1004, "q_norm"),

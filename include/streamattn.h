@@ -95,6 +95,21 @@ int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride,
                  int norm_scope, int rope_style, void* stream);
 
 /*
+ * qk_norm_rope_ex -- qk_norm_rope with a choice of output type.
+ *
+ * out_dtype SA_DTYPE_BF16 is qk_norm_rope. SA_DTYPE_FP8_E4M3 rounds the fp32 results once to
+ * OCP FP8 E4M3 (nearest even; a value past 448 after rounding becomes NaN), the unscaled
+ * float8_e4m3fn cast of the quantized-SDPA option (page "flashdreams.accelerated", section
+ * OptimizedMultiHeadAttention), so q_out and k_out (e.g. an FP8 K cache) hold one byte per
+ * element; their batch strides (elements) must then be multiples of 16.
+ */
+int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride,
+                    const void* k_in, void* k_out, int64_t k_out_bstride,
+                    const float* gamma_q, const float* gamma_k, const float* rope_angles,
+                    int B, int L, int Hq, int Hkv, int d, float eps,
+                    int norm_scope, int rope_style, int out_dtype, void* stream);
+
+/*
  * kv_cache_slot -- rolling sink + window cache: where chunk `chunk_idx` is written and how
  * many cached tokens the chunk then attends to. Pure host integer function (no device work).
  *
@@ -167,6 +182,19 @@ int kv_cache_positions(int64_t chunk_idx, int chunk_len, int sink_size, int wind
 int kv_cache_rope(const void* cache_k, void* k_rot, const float* rope_angles,
                   int B, int Hkv, int d, int chunk_len, int sink_size, int window_size,
                   int64_t chunk_idx, int rope_style, void* stream);
+
+/*
+ * kv_cache_append_ex -- kv_cache_append for caches kept in another element type.
+ *
+ * (src_dtype, cache_dtype): (bf16, bf16), (f16, f16) and (fp8, fp8) copy bytes; (bf16, fp8)
+ * rounds each value to OCP FP8 E4M3 (nearest even, NaN past 448: the quantized-SDPA option
+ * stores its K/V cache in float8_e4m3fn); (bf16, f16) rounds to binary16 (exact for |v| in
+ * [2^-14, 65504]). Any other pair is SA_ERR_UNSUPPORTED. Same slot rule and layout as
+ * kv_cache_append, with one cache element per source element.
+ */
+int kv_cache_append_ex(const void* k_new, const void* v_new, void* cache_k, void* cache_v,
+                       int B, int Lc, int Hkv, int d, int sink_size, int window_size,
+                       int64_t chunk_idx, int src_dtype, int cache_dtype, void* stream);
 
 /*
  * attn_forward -- scaled dot-product attention forward pass, bf16 in and out.

@@ -21,7 +21,7 @@ def widen(t: torch.Tensor) -> np.ndarray:
 
 
 def dtype_name(t: torch.Tensor) -> str:
-    return "bf16" if t.dtype == torch.bfloat16 else "f16"
+    return {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "e4m3"}[t.dtype]
 
 
 def attention_errors(gpu_out: torch.Tensor, ref64: np.ndarray) -> dict:

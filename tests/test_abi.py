@@ -180,3 +180,16 @@ def test_fp8_kv_stride_must_be_16_bytes():
     # 100*4*64 + 8 elements is 16-byte aligned for 16-bit types but not for one-byte FP8
     assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 100 * 4 * 64 + 8, 2, None) == -4
     assert L.attn_forward_kvstride(P, P, P, P, 2, 4, 4, 8, 100, 64, 0.1, 0, 100 * 4 * 64, 3, None) == -3
+
+
+def test_typed_prologue_and_append_reject_bad_arguments():
+    L = lib()
+    P, g = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    # qk_norm_rope_ex: f16 output is not built; FP8 output needs 16-element aligned batch strides
+    assert L.qk_norm_rope_ex(P, P, 128 * 8 * 4, None, None, 0, g, None, g, 1, 4, 8, 0, 128, 1e-6, 1, 1, 1, None) == -3
+    assert L.qk_norm_rope_ex(P, P, 128 * 8 * 4 + 8, None, None, 0, g, None, g, 2, 4, 8, 0, 128, 1e-6, 1, 1, 2,
+                             None) == -2
+    # kv_cache_append_ex: conversions that do not exist
+    assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 1, 2, None) == -3   # f16 -> fp8
+    assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 2, 0, None) == -3   # fp8 -> bf16
+    assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 0, 7, None) == -3   # unknown type

@@ -174,7 +174,7 @@ def test_kv_cache_append_bit_exact_fill_and_eviction(B, Lc, H, d, sink, window):
 
 
 def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, style=binding.SA_ROPE_SPLIT,
-                   after_cache=False, inner=False):
+                   after_cache=False, inner=False, fp8=False):
     """Run the streaming loop on the GPU and compare every chunk's output with the oracle.
 
     Before-cache RoPE: angles at absolute stream positions c*Lc + i rotate the chunk's queries
@@ -182,7 +182,9 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
     unrotated keys; each step rotates the visible keys at their rows 0 .. n-1 of the visible
     sequence (arrival order) and the queries at the last Lc rows."""
     eps, scale = 1e-6, d ** -0.5
-    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after_cache)
+    cdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    rnd = "e4m3" if fp8 else "bf16"   # the type the cache and the attention inputs hold
+    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, dtype=cdt, device=DEV, after_cache_rope=after_cache)
     model = RollingCacheModel(Lc, sink, window)
     g = torch.Generator().manual_seed(seed0)
     gdim = H * d if inner else d
@@ -203,15 +205,15 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
             ang_q = ang[n - Lc:]
         else:
             ang = ang_q = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d)
-        q_buf = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
-        out = torch.empty_like(q_buf)
+        q_buf = torch.empty((B, Lc, H, d), dtype=cdt, device=DEV)
+        out = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
         vis_len = binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, gqd, gkd,
                                                      ang.to(DEV), eps, scale, style, scope)
         torch.cuda.synchronize()
         # oracle: prologue in fp64, rounded once to the bf16 the cache stores; logical window
-        qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang_q, style, inner), "bf16")
-        kstar[c] = oracle.round_to(_oracle_prologue(k, gk, eps, None if after_cache else ang, style, inner), "bf16")
-        vals[c] = widen(v).reshape(v.shape)
+        qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang_q, style, inner), rnd)
+        kstar[c] = oracle.round_to(_oracle_prologue(k, gk, eps, None if after_cache else ang, style, inner), rnd)
+        vals[c] = oracle.round_to(widen(v).reshape(v.shape), rnd)
         vis = model.visible_chunks()
         assert vis_len == n
         K = np.concatenate([kstar[x] for x in vis], axis=1)
@@ -226,9 +228,10 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
             ref = oracle.attention(qs, K, V, scale, rows=rows)
             got = out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)]
         results.append(assert_attention_close(got, ref, f"chunk {c}"))
-        # the cache holds raw V at the model's slot, bit for bit
+        # the cache holds V (rounded to the cache type) at the model's slot, bit for bit
         s0 = model.slot_of(c)
-        assert torch.equal(cache.v[:, s0:s0 + Lc].cpu().view(torch.int16), v.view(torch.int16))
+        got_v = widen(cache.v[:, s0:s0 + Lc]).reshape(v.shape)
+        assert np.array_equal(got_v, vals[c])
     return results
 
 
@@ -272,6 +275,62 @@ def test_streaming_after_cache_full_size_with_sink():
     print(f"[case] after-cache {w}", flush=True)
     _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=w.chunk, window=w.window - w.chunk, n_chunks=6,
                    rows_per_chunk=512, seed0=w.seed + 50, after_cache=True)
+
+
+def test_streaming_fp8_cache_with_sink():
+    # FP8 E4M3 cache: Q and K rounded by the prologue, V by the append; sink + 3-chunk window
+    _streaming_run(B=2, Lc=100, H=4, d=128, sink=100, window=300, n_chunks=7, rows_per_chunk=None, seed0=4600,
+                   fp8=True)
+
+
+def test_streaming_fp8_cache_full_size():
+    """FP8 streaming at full size: 1785 x 40 x 128 chunks, 4-chunk cache; sampled rows."""
+    w = synthetic.WORKLOADS["stream_self_1785x4"]
+    print(f"[case] fp8 {w}", flush=True)
+    _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=0, window=w.window, n_chunks=6, rows_per_chunk=512,
+                   seed0=w.seed + 70, fp8=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("inner", [False, True])
+def test_qk_norm_rope_fp8_output(d, inner):
+    B, L, H = 2, 23, 4
+    g = torch.Generator().manual_seed(300 + d + inner)
+    q = synthetic.normal((B, L, H, d), "bf16", g, 2.0)
+    k = synthetic.normal((B, L, H, d), "bf16", g, 0.5)
+    gq = synthetic.norm_weight(H * d if inner else d, g)
+    gk = synthetic.norm_weight(H * d if inner else d, g)
+    ang = synthetic.rope_angles(np.arange(70, 70 + L), d)
+    qo = torch.empty((B, L, H, d), dtype=torch.float8_e4m3fn, device=DEV)
+    ko = torch.empty_like(qo)
+    binding.qk_norm_rope(q.to(DEV), qo, k.to(DEV), ko, gq.to(DEV), gk.to(DEV), ang.to(DEV), 1e-6,
+                         binding.SA_NORM_INNER if inner else binding.SA_NORM_HEAD, binding.SA_ROPE_SPLIT)
+    torch.cuda.synchronize()
+    assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, oracle.SPLIT, inner), "q e4m3")
+    assert_within_one_ulp(ko, _oracle_prologue(k, gk, 1e-6, ang, oracle.SPLIT, inner), "k e4m3")
+
+
+@pytest.mark.parametrize("cache_dtype", [torch.float8_e4m3fn, torch.float16])
+def test_kv_cache_append_casts_bit_exact(cache_dtype):
+    """bf16 chunks into an E4M3 or f16 cache: each value rounded to nearest even, bit for bit
+    (the oracle rounds the same bf16 values from their exact fp64 form); other rows untouched."""
+    B, Lc, H, d, sink, window = 2, 16, 3, 64, 16, 48
+    S = sink + window
+    name = "e4m3" if cache_dtype == torch.float8_e4m3fn else "f16"
+    cache = torch.zeros((B, S, H, d), dtype=cache_dtype, device=DEV)
+    model = RollingCacheModel(Lc, sink, window)
+    expect = np.zeros((B, S, H, d))
+    g = torch.Generator().manual_seed(17)
+    for c in range(6):
+        v = synthetic.normal((B, Lc, H, d), "bf16", g, 3.0)
+        v[0, 0, 0, :4] = torch.tensor([300.0, -470.0, 1e-4, 65504.0 * 2]).to(torch.bfloat16)  # saturation, subnormal, overflow
+        binding.kv_cache_append(None, v.to(DEV), None, cache, c, sink, window)
+        s0 = model.write(c)
+        expect[:, s0:s0 + Lc] = oracle.round_to(widen(v).reshape(v.shape), name)
+    torch.cuda.synchronize()
+    got = widen(cache).reshape(expect.shape)
+    same = (got == expect) | (np.isnan(got) & np.isnan(expect)) | (np.isinf(got) & np.isinf(expect) & (np.sign(got) == np.sign(expect)))
+    assert same.all(), np.argwhere(~same)[:5]
 
 
 def test_streaming_self_attention_full_size():
