@@ -111,6 +111,9 @@ def make_workload(name: str, dev: str):
         q = synthetic.normal((w.B, w.Lq, w.Hq, w.d), "bf16", g).to(dev)
         k = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g).to(dev)
         v = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g).to(dev)
+        if w.v_cache_dtype:
+            v = v.to(synthetic.DTYPES[w.v_cache_dtype])  # the context cache keeps V in that type
+            info["v_cache_dtype"] = w.v_cache_dtype
         gq = synthetic.norm_weight(w.d, g).to(dev)
         qs = torch.empty_like(q)
         out = torch.empty_like(q)
@@ -128,7 +131,11 @@ def make_workload(name: str, dev: str):
     Lc, S = w.chunk, w.window
     after = w.rope_scope == "after"
     cdt = synthetic.DTYPES[w.cache_dtype]
-    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, dtype=cdt, device=dev, after_cache_rope=after)
+    vdt = synthetic.DTYPES[w.v_cache_dtype] if w.v_cache_dtype else None
+    cache = binding.BlockKVCache(w.B, w.Hkv, w.d, Lc, 0, S, dtype=cdt, device=dev, after_cache_rope=after,
+                                 v_dtype=vdt)
+    if vdt is not None:
+        info["v_cache_dtype"] = w.v_cache_dtype
     g = torch.Generator().manual_seed(w.seed)
     gq, gk = synthetic.norm_weight(w.d, g).to(dev), synthetic.norm_weight(w.d, g).to(dev)
     nsets = 6  # rotate input sets (6 x 55 MB) so the prologue and append are not served from cache

@@ -14,7 +14,7 @@ import torch
 
 from . import build as _build
 
-SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3 = 0, 1, 2
+SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3, SA_DTYPE_BF16_F16V = 0, 1, 2, 3
 SA_ERR_UNSUPPORTED_CODE = -3
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
@@ -87,6 +87,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _attn_dtype(q, k, v) -> int:
+    """Attention dtype code of (q, k, v): one common type, or bf16 q/k with an f16 v."""
+    if q.dtype == torch.bfloat16 and k.dtype == torch.bfloat16 and v.dtype == torch.float16:
+        return SA_DTYPE_BF16_F16V
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError(f"unsupported attention dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    return _dtype_code(q)
+
+
 def attn_forward(q, k, v, out, scale: float, causal: bool = False):
     """out[B, Lq, Hq, d] = softmax(q k^T * scale) v for bf16 q/k/v/out (contiguous)."""
     B, Lq, Hq, d = q.shape
@@ -118,7 +127,7 @@ def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = Fa
     kv_bstride = S * Hkv * d
     _check("attn_forward_kvstride",
            lib().attn_forward_kvstride(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, int(Lk), d,
-                                       float(scale), int(bool(causal)), kv_bstride, _dtype_code(q), _stream(q)))
+                                       float(scale), int(bool(causal)), kv_bstride, _attn_dtype(q, k, v), _stream(q)))
     return out
 
 
@@ -133,7 +142,7 @@ def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk:
     left, right = (int(w) for w in window)
     _check("attn_forward_window",
            lib().attn_forward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
-                                     d, float(scale), left, right, S * Hkv * d, _dtype_code(q), _stream(q)))
+                                     d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _stream(q)))
     return out
 
 
@@ -212,12 +221,15 @@ class BlockKVCache:
     """
 
     def __init__(self, B: int, Hkv: int, d: int, chunk_len: int, sink_size: int, window_size: int,
-                 dtype=torch.bfloat16, device="cuda", after_cache_rope: bool = False):
+                 dtype=torch.bfloat16, device="cuda", after_cache_rope: bool = False, v_dtype=None):
+        """dtype: element type of the cache (bf16, or float8_e4m3fn for the FP8 path). v_dtype=float16
+        with a bf16 cache keeps V in the f16 type the P*V product uses (same results, no per-tile
+        conversion in attention)."""
         self.B, self.Hkv, self.d = B, Hkv, d
         self.chunk_len, self.sink_size, self.window_size = chunk_len, sink_size, window_size
         S = sink_size + window_size
         self.k = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
-        self.v = torch.empty((B, S, Hkv, d), dtype=dtype, device=device)
+        self.v = torch.empty((B, S, Hkv, d), dtype=v_dtype or dtype, device=device)
         # after-cache RoPE: the cache keeps unrotated keys; each step rotates the visible ones here
         self.k_rot = torch.empty_like(self.k) if after_cache_rope else None
         self.slot_base = 0

@@ -43,9 +43,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Input element types (template parameter DT): bf16 or f16 (output in the same type), or FP8
-// E4M3 (OCP float8_e4m3fn, one byte; output bf16).
-constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2;
+// Input element types (template parameter DT): bf16 or f16 (output in the same type), FP8 E4M3
+// (OCP float8_e4m3fn, one byte; output bf16), or bf16 Q/K/out with f16 V (a cache that keeps V
+// in the type the P*V product uses, so no tile is converted).
+constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2, kDtBF16VF16 = 3;
 
 struct KParams {
     const void* q;  // [B, Lq, Hq, D] of the input type; strides below are in its elements
@@ -146,8 +147,9 @@ constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 template <int D, int DT, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr bool FP8 = DT == kDtFP8;
-    constexpr bool BF16 = DT == kDtBF16;        // bf16 operands
-    constexpr bool OUT_BF16 = DT != kDtF16;      // bf16 output
+    constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16;  // bf16 Q and K
+    constexpr bool V_BF16 = DT == kDtBF16;                     // bf16 V, converted to f16 when staged
+    constexpr bool OUT_BF16 = DT != kDtF16;                    // bf16 output
     using In = std::conditional_t<FP8, uint8_t, uint16_t>;
     constexpr int EPC = FP8 ? 16 : 8;            // input elements per 16-byte chunk
     constexpr int kRW = NW / KS;          // row waves per key group
@@ -296,7 +298,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 *reinterpret_cast<u32x4*>(dst) = lo;
                 *reinterpret_cast<u32x4*>(dst + 8) = hi;
             } else {
-                *reinterpret_cast<u32x4*>(dst) = BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+                *reinterpret_cast<u32x4*>(dst) = V_BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
             }
         });
     };
@@ -595,9 +597,11 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 128) {
         if (a.dtype == kDtFP8) return launch_shape<128, kDtFP8>(a, stream);
+        if (a.dtype == kDtBF16VF16) return launch_shape<128, kDtBF16VF16>(a, stream);
         return a.dtype == kDtBF16 ? launch_shape<128, kDtBF16>(a, stream) : launch_shape<128, kDtF16>(a, stream);
     }
     if (a.dtype == kDtFP8) return launch_shape<64, kDtFP8>(a, stream);
+    if (a.dtype == kDtBF16VF16) return launch_shape<64, kDtBF16VF16>(a, stream);
     return a.dtype == kDtBF16 ? launch_shape<64, kDtBF16>(a, stream) : launch_shape<64, kDtF16>(a, stream);
 }
 

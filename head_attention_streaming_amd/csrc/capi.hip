@@ -48,8 +48,9 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lq < 0 || Lk < 0)
         return fail(SA_ERR_RANGE, "attn_forward: negative or zero size (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d)", B, Hq,
                     Hkv, Lq, Lk);
-    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16 && dtype != SA_DTYPE_FP8_E4M3)
-        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0), f16 (1) or fp8 e4m3 (2)", dtype);
+    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16 && dtype != SA_DTYPE_FP8_E4M3 && dtype != SA_DTYPE_BF16_F16V)
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0), f16 (1), fp8 e4m3 (2) or bf16 with f16 v (3)",
+                    dtype);
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward: head dim %d not built (64, 128)", d);
     if (Hq % Hkv != 0) return fail(SA_ERR_SHAPE, "attn_forward: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (win_left < -1 || win_right < -1)

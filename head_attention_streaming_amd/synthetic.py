@@ -83,6 +83,7 @@ class Workload:
     attn_window: tuple | None = None  # local attention band (left, right) around i + Lk - Lq
     rope_scope: str = "before"        # streaming: RoPE before or after the K/V cache update
     cache_dtype: str = "bf16"         # streaming: element type of the K/V cache and attention inputs
+    v_cache_dtype: str | None = None  # V kept in another type (f16: the type P*V uses), same results
 
     @property
     def flops(self) -> float:
@@ -101,12 +102,18 @@ WORKLOADS = {
     # the same streaming step with after-cache RoPE: unrotated cache, visible keys rotated per step
     "stream_after_1785x4": Workload("stream_after_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
                                     128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, rope_scope="after"),
+    # the same streaming step with V cached in f16 (bit-identical outputs, no V conversion in attention)
+    "stream_vf16_1785x4": Workload("stream_vf16_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
+                                   128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, v_cache_dtype="f16"),
     # the same streaming step with an FP8 E4M3 K/V cache (Q, K, V rounded to E4M3, bf16 out)
     "stream_fp8_1785x4": Workload("stream_fp8_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
                                   128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, cache_dtype="e4m3"),
     # cross-attention over a static 512-token context, B = 2 (guidance pair), Q RMSNorm only
     "cross_1785x512": Workload("cross_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
                                128 ** -0.5, 1004, "q_norm"),
+    # the cross-attention context cache with V kept in f16 (bit-identical outputs)
+    "cross_vf16_1785x512": Workload("cross_vf16_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
+                                    128 ** -0.5, 1004, "q_norm", v_cache_dtype="f16"),
     # long non-causal MHA, [1, 20480, 56, 128] bf16
     "mha_20480_bf16": Workload("mha_20480_bf16", 1, 56, 56, 20480, 20480, 128, "bf16", False,
                                128 ** -0.5, 1005),

@@ -46,8 +46,11 @@ typedef enum {
 
 /* Element types. SA_DTYPE_FP8_E4M3 (attention inputs only): OCP FP8 E4M3, the unscaled
  * float8_e4m3fn of the quantized-SDPA option (page "flashdreams.accelerated", section
- * OptimizedMultiHeadAttention); q, k and v are one byte per element, out is bf16. */
-enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1, SA_DTYPE_FP8_E4M3 = 2 };
+ * OptimizedMultiHeadAttention); q, k and v are one byte per element, out is bf16.
+ * SA_DTYPE_BF16_F16V (attention only): q, k and out bf16, v f16 -- for a cache that keeps V in
+ * the f16 type the P*V product uses (kv_cache_append_ex bf16 -> f16); the result is identical to
+ * bf16 v with the same values rounded to f16, minus the per-tile conversion. */
+enum { SA_DTYPE_BF16 = 0, SA_DTYPE_F16 = 1, SA_DTYPE_FP8_E4M3 = 2, SA_DTYPE_BF16_F16V = 3 };
 
 /* Q/K normalisation scope: none, per head (m = d), or inner (m = H*d: all heads of a token). */
 enum { SA_NORM_NONE = 0, SA_NORM_HEAD = 1, SA_NORM_INNER = 2 };
@@ -225,7 +228,8 @@ int attn_forward_f16(const void* q, const void* k, const void* v, void* out,
  * a rolling cache [B, S, Hkv, d] with S >= Lk (streaming self-attention) or a static context
  * cache (cross-attention). kv_bstride is the element distance between batches of k and v
  * (S*Hkv*d for a cache; >= Lk*Hkv*d; a multiple of 16 bytes). dtype is SA_DTYPE_BF16 or
- * SA_DTYPE_F16 for all four tensors, or SA_DTYPE_FP8_E4M3 for q, k and v with a bf16 out.
+ * SA_DTYPE_F16 for all four tensors, SA_DTYPE_FP8_E4M3 for q, k and v with a bf16 out, or
+ * SA_DTYPE_BF16_F16V (bf16 q, k, out; f16 v).
  * FP8: Q K^T runs on the FP8 MFMA with fp32 accumulation from the exact E4M3 values; V is
  * widened exactly to f16 and P V is computed as for 16-bit inputs (f16 probabilities), so the
  * only FP8 rounding is the caller's cast of Q, K and V. Otherwise identical to attn_forward.

@@ -199,3 +199,22 @@ def test_launch_regimes_sampled_rows(idx):
     ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v).reshape(v.shape),
                            scale, causal, rows=rows, window=window)
     assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name)
+
+
+@pytest.mark.parametrize("causal,Lk", [(False, 1111), (True, 700), (False, 90)])
+def test_f16_v_with_bf16_qk_equals_bf16_path(causal, Lk):
+    """bf16 q/k with an f16 v (a cache that keeps V in f16) gives exactly the bf16-v result for
+    the same values (the bf16 path rounds V to f16 itself when staging), and matches the oracle."""
+    B, Lq, H, d = 2, 300 if not causal else Lk, 4, 128
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, H, H, d, "bf16", seed=Lk + causal)
+    v16 = v.to(torch.float16)  # RNE, exact for these values' range
+    qd, kd = q.to(DEV), k.to(DEV)
+    a = torch.empty_like(qd)
+    b = torch.empty_like(qd)
+    binding.attn_forward_kvstride(qd, kd, v16.to(DEV), a, Lk, d ** -0.5, causal)
+    binding.attn_forward_kvstride(qd, kd, v.to(DEV), b, Lk, d ** -0.5, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v16).reshape(v.shape),
+                           d ** -0.5, causal)
+    assert_attention_close(a, ref, "f16 v")

@@ -333,6 +333,29 @@ def test_kv_cache_append_casts_bit_exact(cache_dtype):
     assert same.all(), np.argwhere(~same)[:5]
 
 
+def test_streaming_f16_v_cache_equals_bf16_cache():
+    """A cache that keeps V in f16 (bf16 K) gives bit-identical streaming outputs to a bf16 cache."""
+    B, Lc, H, d, sink, window = 1, 120, 4, 128, 120, 360
+    outs = {}
+    for v_dtype in (None, torch.float16):
+        cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, v_dtype=v_dtype)
+        g = torch.Generator().manual_seed(4700)
+        gq, gk = synthetic.norm_weight(d, g).to(DEV), synthetic.norm_weight(d, g).to(DEV)
+        res = []
+        for c in range(6):
+            gc = torch.Generator().manual_seed(4700 + c)
+            q, k, v = (synthetic.normal((B, Lc, H, d), "bf16", gc).to(DEV) for _ in range(3))
+            ang = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d).to(DEV)
+            q_buf = torch.empty_like(q)
+            out = torch.empty_like(q)
+            binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5)
+            res.append(out.clone())
+        torch.cuda.synchronize()
+        outs[v_dtype] = res
+    for c, (a, b) in enumerate(zip(outs[None], outs[torch.float16])):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"chunk {c}"
+
+
 def test_streaming_self_attention_full_size():
     """Streaming self-attention at full size: chunks of 1785 tokens x 40 heads x 128, rolling cache
     of 4 chunks (7140 keys), chunks 0-5 (fill, then eviction); sampled rows each chunk."""
