@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mha_20480_bf16")
+    p.add_argument("--no-workspace", action="store_true",
+                   help="streaming / cross workloads: plain attention launch instead of the balanced one")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     return p.parse_args()
@@ -61,7 +63,7 @@ def traffic_from_profile(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def make_workload(name: str, dev: str):
+def make_workload(name: str, dev: str, use_ws: bool = True):
     """Build device buffers and return (step_fn, kernel_fn, info)."""
     import numpy as np
     import torch
@@ -117,14 +119,19 @@ def make_workload(name: str, dev: str):
         gq = synthetic.norm_weight(w.d, g).to(dev)
         qs = torch.empty_like(q)
         out = torch.empty_like(q)
+        ws = binding.attn_workspace(w.d, dev) if use_ws else None
+        info["balanced"] = use_ws
+
+        def kern():
+            if ws is not None:
+                binding.attn_forward_ws(qs, k, v, out, w.scale, ws)
+            else:
+                binding.attn_forward_kvstride(qs, k, v, out, w.Lk, w.scale, False)
 
         def step():
             binding.qk_norm_rope(q, qs, None, None, gq, None, None, 1e-6, binding.SA_NORM_HEAD, binding.SA_ROPE_NONE)
-            binding.attn_forward(qs, k, v, out, w.scale, False)
-
-        def kern():
-            binding.attn_forward(qs, k, v, out, w.scale, False)
-        info["step"] = "qk_norm_rope(Q only) + attn_forward"
+            kern()
+        info["step"] = "qk_norm_rope(Q only) + attention" + (" (balanced, workspace)" if ws is not None else "")
         return w, step, kern, info, (q, k, v)
 
     # streaming self-attention: steady state (cache full, every step evicts the oldest chunk)
@@ -152,17 +159,25 @@ def make_workload(name: str, dev: str):
     else:      # absolute stream positions of chunk c
         angles = [synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), w.d).to(dev) for c in range(8)]
 
+    ws = binding.attn_workspace(w.d, dev) if use_ws else None
+    info["balanced"] = use_ws
+
     def step():
         c = state["c"]
         q, k, v = sets[c % nsets]
-        binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[min(c, 7)], 1e-6, w.scale)
+        binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[min(c, 7)], 1e-6, w.scale,
+                                           workspace=ws)
         state["c"] = c + 1
 
     for _ in range(S // Lc):  # fill the cache before timing
         step()
 
     def kern():
-        binding.attn_forward_kvstride(q_buf, cache.k_rot if after else cache.k, cache.v, out, S, w.scale, False)
+        keys = cache.k_rot if after else cache.k
+        if ws is not None:
+            binding.attn_forward_ws(q_buf, keys, cache.v, out, w.scale, ws, Lk=S)
+        else:
+            binding.attn_forward_kvstride(q_buf, keys, cache.v, out, S, w.scale, False)
 
     # the HBM-bound steps alone, on rotating input sets (each set is read once per 6 calls)
     rot = {"i": 0}
@@ -300,7 +315,7 @@ def main():
     import torch
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    w, step, kern, info, tensors = make_workload(args.workload, dev)
+    w, step, kern, info, tensors = make_workload(args.workload, dev, use_ws=not args.no_workspace)
 
     torch.cuda.synchronize()
     if w is None:  # calibration copy: report GB/s only

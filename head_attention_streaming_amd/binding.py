@@ -21,7 +21,7 @@ SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2,
 
 EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
            "kv_cache_append_ex", "kv_cache_rope", "attn_forward", "attn_forward_f16", "attn_forward_kvstride",
-           "attn_forward_window", "sa_last_error")
+           "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "sa_last_error")
 
 _lib = None
 
@@ -56,9 +56,12 @@ def lib():
         L.attn_forward_f16.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
         L.attn_forward_kvstride.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I64, I, P]
         L.attn_forward_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
+        L.attn_forward_workspace_bytes.argtypes = [I]
+        L.attn_forward_ws.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
         L.sa_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = I
+        L.attn_forward_workspace_bytes.restype = I64
         _lib = L
     return _lib
 
@@ -128,6 +131,27 @@ def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = Fa
     _check("attn_forward_kvstride",
            lib().attn_forward_kvstride(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, int(Lk), d,
                                        float(scale), int(bool(causal)), kv_bstride, _attn_dtype(q, k, v), _stream(q)))
+    return out
+
+
+def attn_workspace(d: int, device=None) -> torch.Tensor:
+    """A workspace for attn_forward_ws on the current (or given) device."""
+    n = lib().attn_forward_workspace_bytes(int(d))
+    if n < 0:
+        _check("attn_forward_workspace_bytes", int(n))
+    return torch.empty((int(n),), dtype=torch.uint8, device=device or "cuda")
+
+
+def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None, window=(-1, -1)):
+    """Attention over the first Lk tokens of k, v [B, S, Hkv, d] with a workspace (attn_workspace)
+    that lets under-filled grids run balanced; same results as attn_forward_kvstride."""
+    B, Lq, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    left, right = (int(x) for x in window)
+    _check("attn_forward_ws",
+           lib().attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
+                                 d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(q)))
     return out
 
 
@@ -260,7 +284,7 @@ class BlockKVCache:
 
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
-                               rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD):
+                               rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None):
     """One streaming self-attention chunk as library calls between before_update / after_update.
 
     A cache of float8_e4m3fn (BlockKVCache(dtype=torch.float8_e4m3fn), before-cache RoPE only) with
@@ -273,7 +297,8 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
     logical row; qk_norm_rope rotates q_in with the chunk's rows (the last Lc) and stores the
     normalised keys unrotated -> kv_cache_append -> kv_cache_rope (visible keys -> cache.k_rot)
     -> attn_forward_kvstride over cache.k_rot and the cached values.
-    Returns the visible length used.
+    workspace (attn_workspace): lets the attention run balanced when its grid would leave CU
+    slots idle (attn_forward_ws). Returns the visible length used.
     """
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
@@ -291,6 +316,9 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
         kv_cache_rope(cache.k, cache.k_rot, angles, chunk_idx, cache.chunk_len, cache.sink_size, cache.window_size,
                       rope_style)
         keys = cache.k_rot
-    attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
+    if workspace is not None:
+        attn_forward_ws(q_buf, keys, cache.v, out, scale, workspace, Lk=visible)
+    else:
+        attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
     cache.after_update(chunk_idx)
     return visible

@@ -58,6 +58,12 @@ struct KParams {
     int64_t q_bstride, kv_bstride;
     int q_tstride, kv_tstride;
     float c;  // scale * log2(e)
+    // Balanced launches: each of the sk_wgs workgroups takes sk_full whole units, and the
+    // surplus units from sk_full * sk_wgs on (sk_work = surplus x sk_tiles key tiles) are cut
+    // into sk_wgs equal contiguous pieces whose partial results go to ws (2 slots per workgroup).
+    int sk_tiles, sk_wgs, sk_full;
+    int64_t sk_work;
+    float* ws;
 };
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
@@ -144,7 +150,15 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 template <int D, int RW>
 constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 
-template <int D, int DT, int NW, int KS>
+// Values a lane hands over for one partial unit: its O^T accumulators, the running offset m and
+// its share of the row sum l.
+template <int D>
+constexpr int partial_floats() { return 16 * (D / 32) + 2; }
+
+// Workgroup w of a balanced launch owns surplus positions [w_begin(w), w_begin(w + 1)).
+__device__ __forceinline__ int64_t w_begin(const KParams& p, int w) { return p.sk_work * w / p.sk_wgs; }
+
+template <int D, int DT, int NW, int KS, bool SK>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr bool FP8 = DT == kDtFP8;
     constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16;  // bf16 Q and K
@@ -194,8 +208,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         const int nb = p.nblocks, base = nb >> 3, rem = nb & 7, x = bid & 7;
         bid = x * base + (x < rem ? x : rem) + (bid >> 3);
     }
-    int qblk = bid % p.n_qblk;
-    const int bh = bid / p.n_qblk;
+    // One unit = one (batch, head, query block), over key tiles [seg_ta, seg_tb) when given
+    // (balanced launches; otherwise the tiles the block's rows can see). part_slot >= 0: store
+    // the unnormalised partial result there instead of the output.
+    auto unit = [&](int ubid, int seg_ta, int seg_tb, int part_slot) __attribute__((always_inline)) {
+    int qblk = ubid % p.n_qblk;
+    const int bh = ubid / p.n_qblk;
     const int h = bh % p.Hq;
     const int b = bh / p.Hq;
     if (p.win_right >= 0) qblk = p.n_qblk - 1 - qblk;  // causal-like bands: longest rows first
@@ -212,8 +230,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // row; only those get per-element masks.
     const int kbeg = p.win_left >= 0 ? max(0, qb0 + shift - p.win_left) : 0;
     const int kend = p.win_right >= 0 ? min(p.Lk, qlast + shift + p.win_right + 1) : p.Lk;
-    const int t0 = kbeg / kBN;
-    const int nkt = (kend + kBN - 1) / kBN;
+    const int t0 = SK ? seg_ta : kbeg / kBN;
+    const int nkt = SK ? seg_tb : (kend + kBN - 1) / kBN;
     int tl = t0;
     if (p.win_left >= 0) tl = max(t0, (qlast + shift - p.win_left + kBN - 1) / kBN);
     int tr = p.Lk / kBN;
@@ -509,6 +527,20 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         if (ks == 1) return;
     }
 
+    if constexpr (SK) {
+        if (part_slot >= 0) {  // split unit: hand over O, m, l (merged by attn_merge_kernel)
+            constexpr int NV = partial_floats<D>();
+            float* dst = p.ws + ((int64_t)part_slot * NW + wave) * NV * 64 + lane;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(16 * db + r) * 64] = o[db][r];
+            dst[16 * DB * 64] = m_run;
+            dst[(16 * DB + 1) * 64] = l_run;
+            return;
+        }
+    }
+
     // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
     const float l = half_swap_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -532,6 +564,102 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 *reinterpret_cast<u32x2*>(op + dcol) = w;
             }
     }
+    };  // unit
+
+    if constexpr (SK) {
+        // Balanced launch: this workgroup's whole units, then its piece of the surplus units. A
+        // piece is shorter than one unit's key loop, so it lies in one unit or spans the end of
+        // one and the start of the next: first part -> slot 2w, second part -> slot 2w + 1.
+        for (int i = 0; i < p.sk_full; ++i) unit(bid * p.sk_full + i, 0, p.sk_tiles, -1);
+        const int nT = p.sk_tiles;
+        const int base_unit = p.sk_full * p.sk_wgs;
+        const int64_t w1 = w_begin(p, bid + 1);
+        int slot = 2 * bid;
+        for (int64_t w = w_begin(p, bid); w < w1; ++slot) {
+            const int u = (int)(w / nT), ta = (int)(w % nT);
+            const int tb = (int)min<int64_t>(nT, ta + (w1 - w));
+            unit(base_unit + u, ta, tb, slot);
+            w += tb - ta;
+        }
+    } else {
+        unit(bid, -1, -1, -1);
+    }
+}
+
+// Output of the surplus units of a balanced launch: unit e's key tiles were cut into pieces held
+// by consecutive workgroups; merged in key order, normalised, rounded once.
+template <int D, int DT, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_merge_kernel(KParams p) {
+    constexpr bool OUT_BF16 = DT != kDtF16;
+    constexpr int DB = D / 32;
+    constexpr int NV = partial_floats<D>();
+    constexpr int kBM = NW * 32;
+    const int e = blockIdx.x;
+    const int nT = p.sk_tiles;
+    const int64_t lo = (int64_t)e * nT, hi = lo + nT;  // the unit's surplus positions
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, j = lane & 31;
+    // first workgroup whose piece holds position lo: the last w with w_begin(w) <= lo
+    int w = (int)(lo * p.sk_wgs / p.sk_work);
+    while (w + 1 < p.sk_wgs && w_begin(p, w + 1) <= lo) ++w;
+    while (w > 0 && w_begin(p, w) > lo) --w;
+    float m = -1e30f, l = 0.f;
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    for (; w < p.sk_wgs && w_begin(p, w) < hi; ++w) {
+        if (w_begin(p, w + 1) == w_begin(p, w)) continue;  // empty piece: nothing written
+        // this unit is w's first part if w's piece starts at or after the unit's start
+        const int slot = w_begin(p, w) >= lo ? 2 * w : 2 * w + 1;
+        const float* src = p.ws + ((int64_t)slot * NW + wave) * NV * 64 + lane;
+        const float ms = src[16 * DB * 64];
+        const float mn = fmaxf(m, ms);
+        const float fa = __builtin_amdgcn_exp2f(m - mn), fb = __builtin_amdgcn_exp2f(ms - mn);
+        l = l * fa + src[(16 * DB + 1) * 64] * fb;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + src[(16 * db + r) * 64] * fb;
+        m = mn;
+    }
+    const float lt = half_swap_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int u = p.sk_full * p.sk_wgs + e;
+    const int qblk = u % p.n_qblk, bh = u / p.n_qblk, h = bh % p.Hq, b = bh / p.Hq;
+    const int qrow = qblk * kBM + wave * 32 + j;
+    if (qrow >= p.Lq) return;
+    uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
+            const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
+            u32x2 v;
+            if constexpr (OUT_BF16) {
+                v.x = pack_bf16x2(x0, x1);
+                v.y = pack_bf16x2(x2, x3);
+            } else {
+                v.x = pack_f16x2(x0, x1);
+                v.y = pack_f16x2(x2, x3);
+            }
+            *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * g) = v;
+        }
+}
+
+// Workspace of a balanced launch: two partial slots per workgroup, 4 waves x 64 lanes each.
+int64_t balanced_workspace_bytes(int d, int wgs) {
+    return (int64_t)2 * wgs * 4 * 64 * (16 * (d / 32) + 2) * (int64_t)sizeof(float);
+}
+
+// A balanced launch pays when the plain grid's last round would fill under 90 % of the slots,
+// for full-range attention (every unit the same number of key tiles), more units than slots and
+// key loops of at least 32 tiles (shorter ones spend too much on handing over partial results).
+bool balanced_pays(const AttnArgs& a, int64_t units, int64_t slots, int tiles) {
+    if (a.win_left >= 0 || a.win_right >= 0 || units <= slots || tiles < 32) return false;
+    const int64_t rounds = (units + slots - 1) / slots;
+    return units * 10 < rounds * slots * 9;
 }
 
 int device_cu_count() {
@@ -549,9 +677,9 @@ int device_cu_count() {
 }
 
 template <int D, int DT, int NW, int KS>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+KParams make_params(const AttnArgs& a) {
     constexpr int kBM = NW / KS * 32;
-    KParams p;
+    KParams p{};
     p.q = a.q;
     p.k = a.k;
     p.v = a.v;
@@ -569,9 +697,33 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     p.q_tstride = a.Hq * D;
     p.kv_tstride = a.Hkv * D;
     p.c = a.scale * kLog2e;
-    const int64_t nblocks = (int64_t)p.n_qblk * a.Hq * a.B;
-    p.nblocks = (int)nblocks;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+    p.nblocks = (int)((int64_t)p.n_qblk * a.Hq * a.B);
+    return p;
+}
+
+template <int D, int DT, int NW, int KS>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+    const KParams p = make_params<D, DT, NW, KS>(a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS, false>), dim3((unsigned)p.nblocks), dim3(NW * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Balanced launch of the 4-wave shape: 2 workgroups per CU, each with an equal share of all
+// (unit, key tile) positions, then the merge of the split units.
+template <int D, int DT>
+hipError_t launch_balanced(const AttnArgs& a, int wgs, hipStream_t stream) {
+    constexpr int NW = 4;
+    KParams p = make_params<D, DT, NW, 1>(a);
+    const int units = p.nblocks;
+    p.sk_tiles = (a.Lk + tile_keys<D, NW>() - 1) / tile_keys<D, NW>();
+    p.sk_wgs = wgs;
+    p.sk_full = units / wgs;
+    const int surplus = units - p.sk_full * wgs;  // > 0: balanced_pays requires a partial last round
+    p.sk_work = (int64_t)surplus * p.sk_tiles;
+    p.ws = static_cast<float*>(a.ws);
+    p.nblocks = wgs;  // the XCD regrouping works on the persistent workgroups
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, 1, true>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_merge_kernel<D, DT, NW>), dim3((unsigned)surplus), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -584,15 +736,23 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // pays for [2, 2048, 8, 64] causal (256 workgroups, +15 %), but not for grids above one
     // workgroup per CU (the shared barriers of the two halves cost more than the finer
     // balancing gains) nor for loops of a few tiles (the merge does not amortise).
+    // 4-wave grids whose last round would leave many slots idle (e.g. 560 workgroups on 512
+    // slots) run balanced when the caller passes a workspace.
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
     if (wg256 >= 4 * cus) return launch<D, DT, 8, 1>(a, stream);
     const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
     if (wg128 <= cus && a.Lk >= 512) return launch<D, DT, 8, 2>(a, stream);
+    const int64_t slots = 2 * cus;
+    const int tiles4 = (a.Lk + tile_keys<D, 4>() - 1) / tile_keys<D, 4>();
+    if (balanced_pays(a, wg128, slots, tiles4) && a.ws && a.ws_bytes >= balanced_workspace_bytes(a.d, (int)slots))
+        return launch_balanced<D, DT>(a, (int)slots, stream);
     return launch<D, DT, 4, 1>(a, stream);
 }
 
 }  // namespace
+
+int64_t attn_workspace_bytes(int d) { return balanced_workspace_bytes(d, 2 * device_cu_count()); }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 128) {

@@ -82,11 +82,16 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
 }
 
 int run_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk, int d,
-             float scale, int win_left, int win_right, int64_t kv_bstride, int dtype, void* stream) {
+             float scale, int win_left, int win_right, int64_t kv_bstride, int dtype, void* stream,
+             void* workspace = nullptr, int64_t workspace_bytes = 0) {
     const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, kv_bstride, dtype);
     if (st < 0) return st;
     if (st > 0) return ok();
-    sa::AttnArgs a;
+    if (workspace && (!aligned16(workspace) || workspace_bytes < 0))
+        return fail(SA_ERR_ALIGN, "attn_forward_ws: workspace must be 16-byte aligned");
+    sa::AttnArgs a{};
+    a.ws = workspace;
+    a.ws_bytes = workspace ? workspace_bytes : 0;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -136,6 +141,19 @@ int attn_forward_kvstride(const void* q, const void* k, const void* v, void* out
                           int Lk, int d, float scale, int causal, int64_t kv_bstride, int dtype, void* stream) {
     if (check_causal(causal)) return SA_ERR_RANGE;
     return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, -1, causal ? 0 : -1, kv_bstride, dtype, stream);
+}
+
+int64_t attn_forward_workspace_bytes(int d) {
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward_workspace_bytes: head dim %d not built", d);
+    ok();
+    return sa::attn_workspace_bytes(d);
+}
+
+int attn_forward_ws(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk,
+                    int d, float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                    void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype, stream,
+                    workspace, workspace_bytes);
 }
 
 int attn_forward_window(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,

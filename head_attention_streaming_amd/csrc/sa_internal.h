@@ -18,6 +18,8 @@ struct AttnArgs {
     int win_left;        // visible keys of query i: [i+s-win_left, i+s+win_right], s = Lk - Lq;
     int win_right;       // -1 = unbounded (causal is (-1, 0))
     int dtype;           // SA_DTYPE_*
+    void* ws;            // optional device workspace for balanced launches (null: none)
+    int64_t ws_bytes;
 };
 
 struct NormRopeArgs {
@@ -65,6 +67,7 @@ struct CopyArgs {
 };
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+int64_t attn_workspace_bytes(int d);  // workspace that lets every shape of this device run balanced
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 hipError_t launch_copy_rows(const CopyArgs& a, hipStream_t stream);
 

@@ -258,6 +258,35 @@ int attn_forward_window(const void* q, const void* k, const void* v, void* out,
                         float scale, int window_left, int window_right,
                         int64_t kv_bstride, int dtype, void* stream);
 
+/*
+ * attn_forward_workspace_bytes -- size of the workspace that lets attn_forward_ws balance any
+ * launch of head dim d on the current device (two partial-result slots per persistent
+ * workgroup: 69.2 MB at d = 128 and 35.7 MB at d = 64 on 256 CUs).
+ * Returns the byte count, or SA_ERR_UNSUPPORTED for d not in {64, 128}. Host function.
+ */
+int64_t attn_forward_workspace_bytes(int d);
+
+/*
+ * attn_forward_ws -- attn_forward_window with a caller-provided device workspace.
+ *
+ * Same operation, arguments and results as attn_forward_window (dtype as attn_forward_kvstride;
+ * window (-1, -1) is full attention). The workspace (16-byte aligned device memory of
+ * workspace_bytes, no initialisation needed; NULL or too small: the plain launch) lets grids
+ * whose last round of workgroups would leave many CU slots idle -- e.g. 40 heads x 14 query
+ * blocks = 560 workgroups on 512 slots -- run balanced: one persistent workgroup per slot takes
+ * the same number of whole query blocks, then an equal piece of the key tiles of the remaining
+ * blocks; each piece hands over its partial (O, row maximum, row sum) through the workspace, and
+ * a second kernel merges the pieces of each split block in key order (deterministic, no
+ * atomics). Only for full-range (no causal, no window) attention whose key loop has at least 32
+ * tiles (more than 992 keys at d = 128, 1984 at d = 64); other calls take the plain launch. Whole query
+ * blocks are bit-identical to the plain launch; split ones equal it up to the rounding of the
+ * merge (within the same bounds). Calls that overlap on one workspace race.
+ */
+int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                    float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Text describing the last non-zero status returned to this thread ("" if none). */
 const char* sa_last_error(void);
 

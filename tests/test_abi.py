@@ -26,7 +26,7 @@ pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-side
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
