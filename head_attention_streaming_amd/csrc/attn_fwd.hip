@@ -587,65 +587,100 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 }
 
 // Output of the surplus units of a balanced launch: unit e's key tiles were cut into pieces held
-// by consecutive workgroups; merged in key order, normalised, rounded once.
+// by consecutive workgroups; merged in key order, normalised, rounded once. One workgroup per
+// (unit, 32-feature block), so the partials are read by D/32 times as many CUs; the maximum is
+// taken first so that every piece's loads are independent and several are in flight at once.
 template <int D, int DT, int NW>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_merge_kernel(KParams p) {
+__global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     constexpr bool OUT_BF16 = DT != kDtF16;
     constexpr int DB = D / 32;
     constexpr int NV = partial_floats<D>();
     constexpr int kBM = NW * 32;
-    const int e = blockIdx.x;
-    const int nT = p.sk_tiles;
+    const int e = blockIdx.x / DB, db = blockIdx.x % DB;
+    const int nT = p.sk_tiles, P = p.sk_wgs;
     const int64_t lo = (int64_t)e * nT, hi = lo + nT;  // the unit's surplus positions
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, j = lane & 31;
-    // first workgroup whose piece holds position lo: the last w with w_begin(w) <= lo
-    int w = (int)(lo * p.sk_wgs / p.sk_work);
-    while (w + 1 < p.sk_wgs && w_begin(p, w + 1) <= lo) ++w;
-    while (w > 0 && w_begin(p, w) > lo) --w;
-    float m = -1e30f, l = 0.f;
-    f32x16 o[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    for (; w < p.sk_wgs && w_begin(p, w) < hi; ++w) {
-        if (w_begin(p, w + 1) == w_begin(p, w)) continue;  // empty piece: nothing written
-        // this unit is w's first part if w's piece starts at or after the unit's start
-        const int slot = w_begin(p, w) >= lo ? 2 * w : 2 * w + 1;
-        const float* src = p.ws + ((int64_t)slot * NW + wave) * NV * 64 + lane;
-        const float ms = src[16 * DB * 64];
-        const float mn = fmaxf(m, ms);
-        const float fa = __builtin_amdgcn_exp2f(m - mn), fb = __builtin_amdgcn_exp2f(ms - mn);
-        l = l * fa + src[(16 * DB + 1) * 64] * fb;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + src[(16 * db + r) * 64] * fb;
-        m = mn;
+    // first workgroup whose piece holds position lo: the last w with w_begin(w) <= lo (its piece
+    // is never empty: the next one starts after lo, or it is the last and ends at sk_work > lo)
+    int w0 = (int)(lo * P / p.sk_work);
+    while (w0 + 1 < P && w_begin(p, w0 + 1) <= lo) ++w0;
+    while (w0 > 0 && w_begin(p, w0) > lo) --w0;
+    const int64_t beg0 = w_begin(p, w0);
+    const int rem0 = (int)(p.sk_work * w0 % P);
+    const int64_t step_q = p.sk_work / P;
+    const int step_r = (int)(p.sk_work % P);
+    const float* base = p.ws + (int64_t)wave * NV * 64 + lane;
+    constexpr int64_t kSlot = (int64_t)NW * NV * 64;
+    const float* first = base + (beg0 >= lo ? 2 * w0 : 2 * w0 + 1) * kSlot;
+    // the pieces of workgroups w0, w0 + 1, ... that start before hi, stepping
+    // w_begin(w + 1) = w_begin(w) + step_q (+1 when the remainder of sk_work * w wraps)
+    auto next = [&](int64_t& beg, int& rem) __attribute__((always_inline)) {
+        const int s = rem + step_r;
+        const int64_t nb = beg + step_q + (s >= P ? 1 : 0);
+        rem = s >= P ? s - P : s;
+        return nb;
+    };
+    int n = 0;
+    for (int64_t beg = beg0, rem_ = rem0; w0 + n < P && beg < hi; ++n) {
+        int rem = (int)rem_;
+        beg = next(beg, rem);
+        rem_ = rem;
     }
+    // calls f(src, nonempty) for each of the n pieces; a counted loop with unconditional loads, so
+    // the loads of several pieces are in flight together (an empty piece wrote nothing: it reads
+    // `first`, which always holds a partial, with weight 0)
+    auto each_piece = [&](auto&& f) __attribute__((always_inline)) {
+        int64_t beg = beg0;
+        int rem = rem0;
+#pragma unroll 4
+        for (int i = 0; i < n; ++i) {
+            const int w = w0 + i;
+            const int64_t nb = next(beg, rem);
+            const bool ne = nb > beg;
+            f(ne ? base + (beg >= lo ? 2 * w : 2 * w + 1) * kSlot : first, ne);
+            beg = nb;
+        }
+    };
+    float M = -1e30f;
+    each_piece([&](const float* src, bool ne) {
+        const float mv = src[16 * DB * 64];
+        M = fmaxf(M, ne ? mv : -1e30f);
+    });
+    float l = 0.f;
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.f;
+    each_piece([&](const float* src, bool ne) {
+        const float mv = src[16 * DB * 64], lv = src[(16 * DB + 1) * 64];
+        float ov[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ov[r] = src[(16 * db + r) * 64];
+        const float f = ne ? __builtin_amdgcn_exp2f(mv - M) : 0.f;
+        l += lv * f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] += ov[r] * f;
+    });
     const float lt = half_swap_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int u = p.sk_full * p.sk_wgs + e;
     const int qblk = u % p.n_qblk, bh = u / p.n_qblk, h = bh % p.Hq, b = bh / p.Hq;
     const int qrow = qblk * kBM + wave * 32 + j;
     if (qrow >= p.Lq) return;
-    uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D;
+    uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D + 32 * db;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
-            const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
-            u32x2 v;
-            if constexpr (OUT_BF16) {
-                v.x = pack_bf16x2(x0, x1);
-                v.y = pack_bf16x2(x2, x3);
-            } else {
-                v.x = pack_f16x2(x0, x1);
-                v.y = pack_f16x2(x2, x3);
-            }
-            *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * g) = v;
+    for (int rg = 0; rg < 4; ++rg) {
+        const float x0 = o[4 * rg + 0] * inv, x1 = o[4 * rg + 1] * inv;
+        const float x2 = o[4 * rg + 2] * inv, x3 = o[4 * rg + 3] * inv;
+        u32x2 v;
+        if constexpr (OUT_BF16) {
+            v.x = pack_bf16x2(x0, x1);
+            v.y = pack_bf16x2(x2, x3);
+        } else {
+            v.x = pack_f16x2(x0, x1);
+            v.y = pack_f16x2(x2, x3);
         }
+        *reinterpret_cast<u32x2*>(op + 8 * rg + 4 * g) = v;
+    }
 }
 
 // Workspace of a balanced launch: two partial slots per workgroup, 4 waves x 64 lanes each.
@@ -723,7 +758,8 @@ hipError_t launch_balanced(const AttnArgs& a, int wgs, hipStream_t stream) {
     p.ws = static_cast<float*>(a.ws);
     p.nblocks = wgs;  // the XCD regrouping works on the persistent workgroups
     hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, 1, true>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, p);
-    hipLaunchKernelGGL((attn_merge_kernel<D, DT, NW>), dim3((unsigned)surplus), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_merge_kernel<D, DT, NW>), dim3((unsigned)(surplus * (D / 32))), dim3(NW * 64), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
