@@ -570,16 +570,20 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         // Balanced launch: this workgroup's whole units, then its piece of the surplus units. A
         // piece is shorter than one unit's key loop, so it lies in one unit or spans the end of
         // one and the start of the next: first part -> slot 2w, second part -> slot 2w + 1.
-        for (int i = 0; i < p.sk_full; ++i) unit(bid * p.sk_full + i, 0, p.sk_tiles, -1);
+        // (one loop over both kinds of task, so the unit body is inlined once)
         const int nT = p.sk_tiles;
-        const int base_unit = p.sk_full * p.sk_wgs;
+        int64_t w = w_begin(p, bid);
         const int64_t w1 = w_begin(p, bid + 1);
-        int slot = 2 * bid;
-        for (int64_t w = w_begin(p, bid); w < w1; ++slot) {
-            const int u = (int)(w / nT), ta = (int)(w % nT);
-            const int tb = (int)min<int64_t>(nT, ta + (w1 - w));
-            unit(base_unit + u, ta, tb, slot);
-            w += tb - ta;
+        for (int i = 0, slot = 2 * bid;; ++i) {
+            if (i < p.sk_full) {
+                unit(bid * p.sk_full + i, 0, nT, -1);
+            } else {
+                if (w >= w1) break;
+                const int u = (int)(w / nT), ta = (int)(w % nT);
+                const int tb = (int)min<int64_t>(nT, ta + (w1 - w));
+                unit(p.sk_full * p.sk_wgs + u, ta, tb, slot++);
+                w += tb - ta;
+            }
         }
     } else {
         unit(bid, -1, -1, -1);
@@ -683,14 +687,17 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     }
 }
 
-// Workspace of a balanced launch: two partial slots per workgroup, 4 waves x 64 lanes each.
+// Balanced launches run 8-wave workgroups (256 query rows, 64-key tiles).
+constexpr int kBalancedWaves = 8;
+
+// Workspace of a balanced launch: two partial slots per workgroup, one per wave and lane.
 int64_t balanced_workspace_bytes(int d, int wgs) {
-    return (int64_t)2 * wgs * 4 * 64 * (16 * (d / 32) + 2) * (int64_t)sizeof(float);
+    return (int64_t)2 * wgs * kBalancedWaves * 64 * (16 * (d / 32) + 2) * (int64_t)sizeof(float);
 }
 
-// A balanced launch pays when the plain grid's last round would fill under 90 % of the slots,
-// for full-range attention (every unit the same number of key tiles), more units than slots and
-// key loops of at least 32 tiles (shorter ones spend too much on handing over partial results).
+// A balanced launch pays when the grid's rounds would keep the slots under 90 % busy, for
+// full-range attention (every unit the same number of key tiles), more units than slots and key
+// loops of at least 32 tiles (shorter ones spend too much on handing over partial results).
 bool balanced_pays(const AttnArgs& a, int64_t units, int64_t slots, int tiles) {
     if (a.win_left >= 0 || a.win_right >= 0 || units <= slots || tiles < 32) return false;
     const int64_t rounds = (units + slots - 1) / slots;
@@ -743,11 +750,11 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Balanced launch of the 4-wave shape: 2 workgroups per CU, each with an equal share of all
-// (unit, key tile) positions, then the merge of the split units.
+// Balanced launch: wgs persistent 8-wave workgroups (one per CU), then the merge of the split
+// units.
 template <int D, int DT>
 hipError_t launch_balanced(const AttnArgs& a, int wgs, hipStream_t stream) {
-    constexpr int NW = 4;
+    constexpr int NW = kBalancedWaves;
     KParams p = make_params<D, DT, NW, 1>(a);
     const int units = p.nblocks;
     p.sk_tiles = (a.Lk + tile_keys<D, NW>() - 1) / tile_keys<D, NW>();
@@ -772,23 +779,25 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // pays for [2, 2048, 8, 64] causal (256 workgroups, +15 %), but not for grids above one
     // workgroup per CU (the shared barriers of the two halves cost more than the finer
     // balancing gains) nor for loops of a few tiles (the merge does not amortise).
-    // 4-wave grids whose last round would leave many slots idle (e.g. 560 workgroups on 512
-    // slots) run balanced when the caller passes a workspace.
+    // With a caller workspace, grids of 256-row blocks that would leave the CUs under 90 % busy
+    // over their rounds (e.g. 280 blocks on 256 CUs) run balanced on one persistent 8-wave
+    // workgroup per CU. Measured on MI355X, this beats the plain launches of those grids (also
+    // the 4-wave one, whose last round still gives every CU a workgroup), and beats balancing
+    // 4-wave workgroups: 8 waves per workgroup stage each tile once for twice the rows.
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
+    const int tiles8 = (a.Lk + tile_keys<D, 8>() - 1) / tile_keys<D, 8>();
+    if (a.ws && a.ws_bytes >= balanced_workspace_bytes(a.d, (int)cus) && balanced_pays(a, wg256, cus, tiles8))
+        return launch_balanced<D, DT>(a, (int)cus, stream);
     if (wg256 >= 4 * cus) return launch<D, DT, 8, 1>(a, stream);
     const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
     if (wg128 <= cus && a.Lk >= 512) return launch<D, DT, 8, 2>(a, stream);
-    const int64_t slots = 2 * cus;
-    const int tiles4 = (a.Lk + tile_keys<D, 4>() - 1) / tile_keys<D, 4>();
-    if (balanced_pays(a, wg128, slots, tiles4) && a.ws && a.ws_bytes >= balanced_workspace_bytes(a.d, (int)slots))
-        return launch_balanced<D, DT>(a, (int)slots, stream);
     return launch<D, DT, 4, 1>(a, stream);
 }
 
 }  // namespace
 
-int64_t attn_workspace_bytes(int d) { return balanced_workspace_bytes(d, 2 * device_cu_count()); }
+int64_t attn_workspace_bytes(int d) { return balanced_workspace_bytes(d, device_cu_count()); }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 128) {

@@ -261,7 +261,7 @@ int attn_forward_window(const void* q, const void* k, const void* v, void* out,
 /*
  * attn_forward_workspace_bytes -- size of the workspace that lets attn_forward_ws balance any
  * launch of head dim d on the current device (two partial-result slots per persistent
- * workgroup: 69.2 MB at d = 128 and 35.7 MB at d = 64 on 256 CUs).
+ * workgroup, one workgroup per CU: 69.2 MB at d = 128 and 35.7 MB at d = 64 on 256 CUs).
  * Returns the byte count, or SA_ERR_UNSUPPORTED for d not in {64, 128}. Host function.
  */
 int64_t attn_forward_workspace_bytes(int d);
@@ -272,14 +272,14 @@ int64_t attn_forward_workspace_bytes(int d);
  * Same operation, arguments and results as attn_forward_window (dtype as attn_forward_kvstride;
  * window (-1, -1) is full attention). The workspace (16-byte aligned device memory of
  * workspace_bytes, no initialisation needed; NULL or too small: the plain launch) lets grids
- * whose last round of workgroups would leave many CU slots idle -- e.g. 40 heads x 14 query
- * blocks = 560 workgroups on 512 slots -- run balanced: one persistent workgroup per slot takes
+ * of 256-row query blocks whose rounds would keep the CUs under 90 % busy -- e.g. 40 heads x 7
+ * blocks = 280 blocks on 256 CUs -- run balanced: one persistent 8-wave workgroup per CU takes
  * the same number of whole query blocks, then an equal piece of the key tiles of the remaining
  * blocks; each piece hands over its partial (O, row maximum, row sum) through the workspace, and
  * a second kernel merges the pieces of each split block in key order (deterministic, no
  * atomics). Only for full-range (no causal, no window) attention whose key loop has at least 32
- * tiles (more than 992 keys at d = 128, 1984 at d = 64); other calls take the plain launch. Whole query
- * blocks are bit-identical to the plain launch; split ones equal it up to the rounding of the
+ * tiles of 64 keys (Lk > 1984); other calls take the plain launch. Whole query blocks are
+ * computed exactly as by the 8-wave plain launch; split ones equal it up to the rounding of the
  * merge (within the same bounds). Calls that overlap on one workspace race.
  */
 int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
