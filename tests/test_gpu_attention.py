@@ -141,10 +141,12 @@ def test_empty_query_is_noop():
 
 
 WIDE_CASES = [
-    # enough (batch, head, 256-row block) workgroups to select the 8-wave launch shape
+    # at least four (batch, head, 256-row block) workgroups per CU: the 8-wave launch shape,
+    # except causal rows of at most 4096 keys, which run 128-row blocks of 4 waves
     ("wide_ragged_bf16_d128", 1, 4000, 333, 64, 64, 128, "bf16", False),
     ("wide_causal_f16_d64", 2, 2000, 2000, 64, 64, 64, "f16", True),
     ("wide_gqa_causal_bf16_d128", 4, 1000, 1100, 64, 8, 128, "bf16", True),
+    ("wide_long_causal_8wave_bf16_d128", 1, 4500, 4600, 64, 16, 128, "bf16", True),
 ]
 
 

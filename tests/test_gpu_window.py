@@ -80,9 +80,11 @@ def test_window_over_prefix_of_larger_buffer():
 
 
 WIDE_CASES = [
-    # enough 256-row workgroups for the 8-wave launch shape
+    # at least four 256-row blocks per CU: bands of at most 2049 keys run 128-row blocks of 4
+    # waves, wider ones 256-row blocks of 8 waves
     ("wide_sliding_1024_bf16_d128", 1, 8192, 8192, 32, 32, 128, "bf16", (1024, 0)),
     ("wide_symmetric_f16_d64", 2, 4000, 4000, 32, 8, 64, "f16", (700, 300)),
+    ("wide_band_3101_8wave_bf16_d128", 1, 8192, 8192, 32, 32, 128, "bf16", (2500, 600)),
 ]
 
 
