@@ -155,10 +155,18 @@ constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 template <int D>
 constexpr int partial_floats() { return 16 * (D / 32) + 2; }
 
+// Integer min / max of 64-bit values (in device code the generic min / max of int64_t go through
+// double precision).
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
 // Workgroup w of a balanced launch owns surplus positions [w_begin(w), w_begin(w + 1)).
 __device__ __forceinline__ int64_t w_begin(const KParams& p, int w) { return p.sk_work * w / p.sk_wgs; }
 
-template <int D, int DT, int NW, int KS, bool SK>
+template <int D, int DT, int NW, int KS, bool SK, bool BIG>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr bool FP8 = DT == kDtFP8;
     constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16;  // bf16 Q and K
@@ -195,7 +203,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform over the wave: say so, so that values derived from it (the key
+    // group, its tile indices, the buffer offsets) stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ks = KS == 1 ? 0 : wave / kRW;     // key group of this wave
     const int rw = KS == 1 ? wave : wave % kRW;  // row wave within the group
     const int g = lane >> 5;   // half of the wave
@@ -247,8 +257,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     int key_lo, key_hi;
     {
         const int64_t pos = (int64_t)qrow + shift;
-        key_lo = p.win_left >= 0 ? (int)max<int64_t>(0, pos - p.win_left) : 0;
-        key_hi = p.win_right >= 0 ? (int)min<int64_t>(p.Lk - 1, pos + p.win_right) : p.Lk - 1;
+        key_lo = p.win_left >= 0 ? (int)max64(0, pos - p.win_left) : 0;
+        key_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, pos + p.win_right) : p.Lk - 1;
     }
     const unsigned key_span = (unsigned)(key_hi - key_lo);
 
@@ -279,27 +289,47 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     const int tid_g = KS == 1 ? tid : tid % kGThreads;
     const bool stager = kChunks >= kGThreads || tid_g < kChunks;
     const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * EPC;
-    const In* kg = pk + b * p.kv_bstride + hk * D + scol;
-    const In* vg = pv + b * p.kv_bstride + hk * D + scol;
+    // K and V rows of this (batch, K/V head) are read through buffer resources that end at row
+    // Lk: rows at or past Lk fall outside the range and read as zero (their scores are masked).
+    // A thread's byte offset is a constant plus the tile's first row; when the rows up to one
+    // tile past Lk span 4 GiB or more (BIG), each tile gets a resource rebased at its first row
+    // instead, so every offset stays within 32 bits.
+    const char* const kbase = reinterpret_cast<const char*>(pk + b * p.kv_bstride + hk * D);
+    const char* const vbase = reinterpret_cast<const char*>(pv + b * p.kv_bstride + hk * D);
+    const uint32_t row_bytes = (uint32_t)p.kv_tstride * (uint32_t)sizeof(In);
+    const uint32_t tile_bytes = (uint32_t)kBN * row_bytes;
+    const uint32_t voff0 = (uint32_t)srow0 * row_bytes + (uint32_t)(scol * sizeof(In));
+    const uint32_t region_bytes = BIG ? 0u : (uint32_t)p.Lk * row_bytes;
+    const auto k_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)region_bytes, kBufferWord3);
+    const auto v_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)region_bytes, kBufferWord3);
+    auto tile_rsrc = [&](const char* base, int kt) __attribute__((always_inline)) {
+        const int64_t row0 = (int64_t)kt * kBN;
+        const int64_t bytes = min64(max64(0, p.Lk - row0) * row_bytes, 0xffffffffLL);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + row0 * row_bytes), (short)0,
+                                                  (int)(uint32_t)bytes, kBufferWord3);
+    };
     In* const Kg = &Ks[ks][0];  // this group's K and V slots (V always f16 in LDS)
     uint16_t* const Vg = &Vs[ks][0];
     In* ks_st = Kg + srow0 * KST + scol;
     uint16_t* vs_st = Vg + srow0 * VST + scol;
     u32x4 kreg[NCH], vreg[NCH];
-    auto load_k = [&](int kt) __attribute__((always_inline)) {
+    auto load_rows = [&](u32x4 (&dst)[NCH], const char* base, const __amdgpu_buffer_rsrc_t& whole, int kt)
+                         __attribute__((always_inline)) {
         if (!stager) return;
-        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
-            kreg[u] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * p.kv_tstride);
-        });
+        if constexpr (!BIG) {
+            const uint32_t toff = (uint32_t)kt * tile_bytes;
+            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(whole, voff0 + (toff + (uint32_t)(u * RSTEP) * row_bytes), 0, 0);
+            });
+        } else {
+            const auto r = tile_rsrc(base, kt);
+            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff0 + (uint32_t)(u * RSTEP) * row_bytes, 0, 0);
+            });
+        }
     };
-    auto load_v = [&](int kt) __attribute__((always_inline)) {
-        if (!stager) return;
-        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            const int key = min(kt * kBN + srow0 + u * RSTEP, p.Lk - 1);
-            vreg[u] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * p.kv_tstride);
-        });
-    };
+    auto load_k = [&](int kt) __attribute__((always_inline)) { load_rows(kreg, kbase, k_rsrc, kt); };
+    auto load_v = [&](int kt) __attribute__((always_inline)) { load_rows(vreg, vbase, v_rsrc, kt); };
     auto store_k = [&](int slot) __attribute__((always_inline)) {
         if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
@@ -580,7 +610,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             } else {
                 if (w >= w1) break;
                 const int u = (int)(w / nT), ta = (int)(w % nT);
-                const int tb = (int)min<int64_t>(nT, ta + (w1 - w));
+                const int tb = (int)min64(nT, ta + (w1 - w));
                 unit(p.sk_full * p.sk_wgs + u, ta, tb, slot++);
                 w += tb - ta;
             }
@@ -743,10 +773,10 @@ KParams make_params(const AttnArgs& a) {
     return p;
 }
 
-template <int D, int DT, int NW, int KS>
+template <int D, int DT, int NW, int KS, bool BIG = false>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
     const KParams p = make_params<D, DT, NW, KS>(a);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS, false>), dim3((unsigned)p.nblocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS, false, BIG>), dim3((unsigned)p.nblocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -764,7 +794,7 @@ hipError_t launch_balanced(const AttnArgs& a, int wgs, hipStream_t stream) {
     p.sk_work = (int64_t)surplus * p.sk_tiles;
     p.ws = static_cast<float*>(a.ws);
     p.nblocks = wgs;  // the XCD regrouping works on the persistent workgroups
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, 1, true>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, 1, true, false>), dim3((unsigned)wgs), dim3(NW * 64), 0, stream, p);
     hipLaunchKernelGGL((attn_merge_kernel<D, DT, NW>), dim3((unsigned)(surplus * (D / 32))), dim3(NW * 64), 0,
                        stream, p);
     return hipGetLastError();
@@ -784,6 +814,10 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // workgroup per CU. Measured on MI355X, this beats the plain launches of those grids (also
     // the 4-wave one, whose last round still gives every CU a workgroup), and beats balancing
     // 4-wave workgroups: 8 waves per workgroup stage each tile once for twice the rows.
+    // K/V regions whose rows up to one tile past Lk span 4 GiB or more: the plain 8-wave shape
+    // with per-tile buffer resources (any grid)
+    const int64_t elem = DT == kDtFP8 ? 1 : 2;
+    if (((int64_t)a.Lk + 64) * a.Hkv * D * elem > 0xffffffffLL) return launch<D, DT, 8, 1, true>(a, stream);
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
     const int tiles8 = (a.Lk + tile_keys<D, 8>() - 1) / tile_keys<D, 8>();

@@ -220,3 +220,26 @@ def test_f16_v_with_bf16_qk_equals_bf16_path(causal, Lk):
     ref = oracle.attention(widen(q).reshape(q.shape), widen(k).reshape(k.shape), widen(v16).reshape(v.shape),
                            d ** -0.5, causal)
     assert_attention_close(a, ref, "f16 v")
+
+
+def test_kv_region_past_4gib_uses_rebased_resources():
+    """K/V regions whose rows (up to one tile past Lk) span 4 GiB or more: 64 K/V heads x 262200
+    keys x 128 features of bf16 = 4.3 GB per tensor. Every head's rows are read through 32-bit
+    buffer offsets from a base that moves with the tile; three heads are checked against the
+    oracle on their own slices (all 40 query rows, every key, ragged last tile)."""
+    B, Lq, Lk, H, d = 1, 40, 262200, 64, 128
+    assert (Lk + 64) * H * d * 2 > 0xFFFFFFFF
+    print(f"[case] big region B={B} Lq={Lq} Lk={Lk} H={H} d={d} bf16", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(4242)
+    q = torch.randn((B, Lq, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn((B, Lk, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((B, Lk, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    binding.attn_forward(q, k, v, out, d ** -0.5, False)
+    torch.cuda.synchronize()
+    for h in (0, 37, 63):
+        qh, kh, vh = (t[:, :, h:h + 1].contiguous().cpu() for t in (q, k, v))
+        ref = oracle.attention(widen(qh).reshape(qh.shape), widen(kh).reshape(kh.shape),
+                               widen(vh).reshape(vh.shape), d ** -0.5)
+        assert_attention_close(out[:, :, h:h + 1].contiguous(), ref, f"big region head {h}")
+    del k, v
