@@ -117,21 +117,15 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
             v = v.to(synthetic.DTYPES[w.v_cache_dtype])  # the context cache keeps V in that type
             info["v_cache_dtype"] = w.v_cache_dtype
         gq = synthetic.norm_weight(w.d, g).to(dev)
-        qs = torch.empty_like(q)
         out = torch.empty_like(q)
         ws = binding.attn_workspace(w.d, dev) if use_ws else None
         info["balanced"] = use_ws
 
-        def kern():
-            if ws is not None:
-                binding.attn_forward_ws(qs, k, v, out, w.scale, ws)
-            else:
-                binding.attn_forward_kvstride(qs, k, v, out, w.Lk, w.scale, False)
+        def kern():  # the Q RMSNorm is fused into the attention kernel's query load
+            binding.attn_forward_qnorm(q, k, v, out, w.scale, gq, 1e-6, workspace=ws)
 
-        def step():
-            binding.qk_norm_rope(q, qs, None, None, gq, None, None, 1e-6, binding.SA_NORM_HEAD, binding.SA_ROPE_NONE)
-            kern()
-        info["step"] = "qk_norm_rope(Q only) + attention" + (" (balanced, workspace)" if ws is not None else "")
+        step = kern
+        info["step"] = "attention with the Q RMSNorm fused into its query load (attn_forward_qnorm)"
         return w, step, kern, info, (q, k, v)
 
     # streaming self-attention: steady state (cache full, every step evicts the oldest chunk)

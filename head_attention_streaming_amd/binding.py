@@ -21,7 +21,8 @@ SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2,
 
 EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
            "kv_cache_append_ex", "kv_cache_rope", "attn_forward", "attn_forward_f16", "attn_forward_kvstride",
-           "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "sa_last_error")
+           "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "attn_forward_qnorm",
+           "sa_last_error")
 
 _lib = None
 
@@ -58,6 +59,7 @@ def lib():
         L.attn_forward_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
         L.attn_forward_workspace_bytes.argtypes = [I]
         L.attn_forward_ws.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
+        L.attn_forward_qnorm.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
         L.sa_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = I
@@ -152,6 +154,22 @@ def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None
            lib().attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
                                  d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
+    return out
+
+
+def attn_forward_qnorm(q, k, v, out, scale: float, gamma_q, eps: float = 1e-6, workspace=None, Lk: int | None = None,
+                       window=(-1, -1)):
+    """Attention whose query rows are RMS-normalised (head scope, weights gamma_q fp32 [d]) as
+    they are loaded; q itself is not modified. Same as qk_norm_rope (Q only, no RoPE) followed by
+    attn_forward_ws, without the normalised Q round trip through memory."""
+    B, Lq, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    left, right = (int(x) for x in window)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("attn_forward_qnorm",
+           lib().attn_forward_qnorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(gamma_q), float(eps), B, Hq, Hkv, Lq,
+                                    S if Lk is None else int(Lk), d, float(scale), left, right, S * Hkv * d,
+                                    _attn_dtype(q, k, v), _ptr(workspace), ws_bytes, _stream(q)))
     return out
 
 

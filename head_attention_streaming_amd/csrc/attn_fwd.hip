@@ -33,6 +33,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes as a native vector
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
@@ -64,6 +65,10 @@ struct KParams {
     int sk_tiles, sk_wgs, sk_full;
     int64_t sk_work;
     float* ws;
+    // Optional RMSNorm of every query row (head scope) applied as it is loaded: weights [D]
+    // (null: queries are used as given) and epsilon.
+    const float* gamma_q;
+    float q_eps;
 };
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
@@ -279,6 +284,45 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 qf[c] = __builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}));
             } else {
                 qf[c] = *reinterpret_cast<const u32x4*>(qp + 16 * c);
+            }
+        }
+    }
+    if constexpr (!FP8) {
+        if (p.gamma_q) {  // uniform. RMSNorm of the query row, then one rounding to the input type:
+            // gamma * (z * r), r = 1 / sqrt(mean(z^2) + eps); this lane holds half of the row's
+            // features, lane j + 32 (or j - 32) the other half
+            float z[DC][8];
+            float ss = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                const uint32_t w[4] = {qf[cc].x, qf[cc].y, qf[cc].z, qf[cc].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (BF16) {
+                        z[cc][2 * i] = __uint_as_float(w[i] << 16);
+                        z[cc][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                    } else {
+                        const f16x2 h2 = __builtin_bit_cast(f16x2, w[i]);
+                        z[cc][2 * i] = (float)h2[0];
+                        z[cc][2 * i + 1] = (float)h2[1];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += z[cc][e] * z[cc][e];
+            }
+            const float r = 1.f / sqrtf(half_swap_sum(ss) / (float)D + p.q_eps);
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
+                const f32x4* gp = reinterpret_cast<const f32x4*>(p.gamma_q + 16 * cc + 8 * g);
+                const f32x4 g0 = gp[0], g1 = gp[1];
+                const float gw[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = gw[2 * i] * (z[cc][2 * i] * r), x1 = gw[2 * i + 1] * (z[cc][2 * i + 1] * r);
+                    w[i] = BF16 ? pack_bf16x2(x0, x1) : pack_f16x2(x0, x1);
+                }
+                qf[cc] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
     }
@@ -769,6 +813,8 @@ KParams make_params(const AttnArgs& a) {
     p.q_tstride = a.Hq * D;
     p.kv_tstride = a.Hkv * D;
     p.c = a.scale * kLog2e;
+    p.gamma_q = a.gamma_q;
+    p.q_eps = a.q_eps;
     p.nblocks = (int)((int64_t)p.n_qblk * a.Hq * a.B);
     return p;
 }

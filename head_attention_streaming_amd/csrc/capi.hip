@@ -83,7 +83,8 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
 
 int run_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk, int d,
              float scale, int win_left, int win_right, int64_t kv_bstride, int dtype, void* stream,
-             void* workspace = nullptr, int64_t workspace_bytes = 0) {
+             void* workspace = nullptr, int64_t workspace_bytes = 0, const float* gamma_q = nullptr,
+             float q_eps = 0.f) {
     const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, kv_bstride, dtype);
     if (st < 0) return st;
     if (st > 0) return ok();
@@ -110,6 +111,8 @@ int run_attn(const void* q, const void* k, const void* v, void* out, int B, int 
     a.win_left = win_left >= Lk - 1 ? -1 : win_left;
     a.win_right = win_right >= Lq - 1 ? -1 : win_right;
     a.dtype = dtype;
+    a.gamma_q = gamma_q;
+    a.q_eps = q_eps;
     return hip_status(sa::launch_attn_fwd(a, static_cast<hipStream_t>(stream)), "attn_forward launch");
 }
 
@@ -154,6 +157,18 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out, int 
                     void* workspace, int64_t workspace_bytes, void* stream) {
     return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype, stream,
                     workspace, workspace_bytes);
+}
+
+int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, const float* gamma_q, float eps,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale, int window_left, int window_right,
+                       int64_t kv_bstride, int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!gamma_q) return fail(SA_ERR_NULL, "attn_forward_qnorm: gamma_q is null");
+    if (!aligned16(gamma_q)) return fail(SA_ERR_ALIGN, "attn_forward_qnorm: gamma_q must be 16-byte aligned");
+    if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "attn_forward_qnorm: eps must be >= 0 and finite");
+    if (dtype == SA_DTYPE_FP8_E4M3)
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward_qnorm: the fused query norm takes 16-bit queries");
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype, stream,
+                    workspace, workspace_bytes, gamma_q, eps);
 }
 
 int attn_forward_window(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,

@@ -20,6 +20,8 @@ struct AttnArgs {
     int dtype;           // SA_DTYPE_*
     void* ws;            // optional device workspace for balanced launches (null: none)
     int64_t ws_bytes;
+    const float* gamma_q;  // optional RMSNorm weights [d] applied to each query row (null: none)
+    float q_eps;
 };
 
 struct NormRopeArgs {

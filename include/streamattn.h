@@ -287,6 +287,25 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
                     float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * attn_forward_qnorm -- attn_forward_ws with the query RMSNorm (head scope) fused into the
+ * attention: each query row z is replaced by gamma_q * z / sqrt(mean(z^2) + eps), rounded once to
+ * the query type, as it is loaded, and attended with. Page "flashdreams.accelerated", section
+ * "Multi Head Attention Definition" (RMSNorm of Q before attention, per head; no RoPE here: the
+ * cross-attention example normalises Q only) and equation of the attention itself there.
+ *
+ * q is read as given and not modified; the result equals qk_norm_rope(q, NORM_HEAD, ROPE_NONE)
+ * followed by attn_forward_ws up to the summation order of the row's sum of squares (the
+ * normalised query can differ by one ulp of the query type in rare rounding ties). gamma_q:
+ * fp32 [d], 16-byte aligned, device memory. eps >= 0 and finite. dtype SA_DTYPE_BF16, SA_DTYPE_F16
+ * or SA_DTYPE_BF16_F16V (FP8 queries: SA_ERR_UNSUPPORTED). Every other argument, the workspace
+ * (may be NULL) and the errors as attn_forward_ws.
+ */
+int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, const float* gamma_q, float eps,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale, int window_left,
+                       int window_right, int64_t kv_bstride, int dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
 /* Text describing the last non-zero status returned to this thread ("" if none). */
 const char* sa_last_error(void);
 

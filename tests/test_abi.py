@@ -200,3 +200,22 @@ def test_typed_prologue_and_append_reject_bad_arguments():
     assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 1, 2, None) == -3   # f16 -> fp8
     assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 2, 0, None) == -3   # fp8 -> bf16
     assert L.kv_cache_append_ex(None, P, None, P, 1, 16, 2, 64, 0, 64, 0, 0, 7, None) == -3   # unknown type
+
+
+def test_attn_forward_qnorm_rejects_bad_arguments():
+    L = lib()
+    P, g = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+
+    def call(gamma=g, eps=1e-6, Hq=8, Hkv=8, dtype=0, d=128):
+        return L.attn_forward_qnorm(P, P, P, P, gamma, eps, 1, Hq, Hkv, 16, 16, d, 0.1, -1, -1, 16 * Hkv * d, dtype,
+                                    None, 0, None)
+
+    assert call(gamma=None) == -1
+    assert call(gamma=ctypes.c_void_p(8192 + 4)) == -4
+    assert call(eps=-1.0) == -5
+    assert call(eps=float("nan")) == -5
+    assert call(dtype=2) == -3          # FP8 queries: no fused norm
+    assert call(dtype=9) == -3
+    assert call(Hq=6, Hkv=4) == -2
+    assert call(d=96) == -3
+    assert lib().sa_last_error().decode() != ""

@@ -387,3 +387,74 @@ def test_cross_attention_full_size():
     rows = sample_rows(w.B, w.Lq, w.Hq, 4096, seed=3)
     ref = oracle.attention(q_ref, widen(k).reshape(k.shape), widen(v).reshape(v.shape), w.scale, rows=rows)
     assert_attention_close(out.reshape(-1, w.d)[torch.from_numpy(rows).to(DEV)], ref, w.name)
+
+
+FUSED_QNORM_CASES = [
+    # name, B, Lq, Lk, Hq, Hkv, d, q/k dtype, v dtype, window, workspace
+    ("qnorm_bf16_d128_ragged", 2, 300, 200, 4, 2, 128, "bf16", "bf16", (-1, -1), False),
+    ("qnorm_f16_d64", 1, 257, 513, 3, 3, 64, "f16", "f16", (-1, -1), False),
+    ("qnorm_window_bf16_d128", 1, 400, 400, 2, 2, 128, "bf16", "bf16", (100, 0), False),
+    ("qnorm_bf16qk_f16v_d128", 1, 200, 300, 4, 4, 128, "bf16", "f16", (-1, -1), False),
+    ("qnorm_wide_grid_bf16_d128", 1, 4000, 333, 64, 16, 128, "bf16", "bf16", (-1, -1), False),
+    ("qnorm_balanced_stream_shape", 1, 1785, 7140, 40, 40, 128, "bf16", "bf16", (-1, -1), True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_QNORM_CASES, ids=[c[0] for c in FUSED_QNORM_CASES])
+def test_attention_with_fused_query_norm_matches_oracle(case):
+    """attn_forward_qnorm: each query row is RMS-normalised (head scope) and rounded once as it
+    is loaded; compared with the oracle's normalised query, rounded once, then attention."""
+    name, B, Lq, Lk, Hq, Hkv, d, qk_dt, v_dt, window, use_ws = case
+    print(f"[case] {case}", flush=True)
+    g = torch.Generator().manual_seed(zlib_seed(name))
+    q = synthetic.normal((B, Lq, Hq, d), qk_dt, g, 2.0)
+    k = synthetic.normal((B, Lk, Hkv, d), qk_dt, g)
+    v = synthetic.normal((B, Lk, Hkv, d), v_dt, g)
+    gq = synthetic.norm_weight(d, g)
+    qd = q.to(DEV)
+    q_before = qd.clone()
+    out = torch.empty_like(qd)
+    ws = binding.attn_workspace(d) if use_ws else None
+    binding.attn_forward_qnorm(qd, k.to(DEV), v.to(DEV), out, d ** -0.5, gq.to(DEV), 1e-6, workspace=ws,
+                               window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.view(torch.int16), q_before.view(torch.int16)), "q must not be modified"
+    q_ref = oracle.round_to(_oracle_prologue(q, gq, 1e-6, None, 0), qk_dt)
+    win = None if window == (-1, -1) else window
+    rows = sample_rows(B, Lq, Hq, 3000, seed=5) if B * Lq * Hq > 20000 else None
+    ref = oracle.attention(q_ref, widen(k).reshape(k.shape), widen(v).reshape(v.shape), d ** -0.5, rows=rows,
+                           window=win)
+    got = out if rows is None else out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)]
+    assert_attention_close(got, ref, name)
+
+
+def test_cross_attention_fused_query_norm_full_size():
+    """The cross-attention configuration (B=2, 40 heads, 1785 queries over a 512-token context)
+    with the Q RMSNorm fused into the attention: sampled rows against the oracle, and every
+    output within the attention bounds of the two-kernel path (prologue, then attention)."""
+    w = synthetic.WORKLOADS["cross_1785x512"]
+    print(f"[case] fused {w}", flush=True)
+    g = torch.Generator().manual_seed(w.seed)
+    q = synthetic.normal((w.B, w.Lq, w.Hq, w.d), "bf16", g)
+    k = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g)
+    v = synthetic.normal((w.B, w.Lk, w.Hkv, w.d), "bf16", g)
+    gq = synthetic.norm_weight(w.d, g)
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), gq.to(DEV)
+    fused = torch.empty_like(qd)
+    binding.attn_forward_qnorm(qd, kd, vd, fused, w.scale, gd, 1e-6)
+    qs = torch.empty_like(qd)
+    binding.qk_norm_rope(qd, qs, None, None, gd, None, None, 1e-6, binding.SA_NORM_HEAD, binding.SA_ROPE_NONE)
+    two = torch.empty_like(qd)
+    binding.attn_forward(qs, kd, vd, two, w.scale, False)
+    torch.cuda.synchronize()
+    diff = (fused.float() - two.float()).abs()
+    assert diff.max().item() <= 8e-3 and diff.mean().item() <= 1e-4, (diff.max().item(), diff.mean().item())
+    q_ref = oracle.round_to(_oracle_prologue(q, gq, 1e-6, None, 0), "bf16")
+    rows = sample_rows(w.B, w.Lq, w.Hq, 4096, seed=4)
+    ref = oracle.attention(q_ref, widen(k).reshape(k.shape), widen(v).reshape(v.shape), w.scale, rows=rows)
+    assert_attention_close(fused.reshape(-1, w.d)[torch.from_numpy(rows).to(DEV)], ref, "fused " + w.name)
+
+
+def zlib_seed(name: str) -> int:
+    import zlib
+    return zlib.crc32(name.encode()) % 10000
