@@ -155,10 +155,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 template <int D, int RW>
 constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
 
-// Values a lane hands over for one partial unit: its O^T accumulators, the running offset m and
-// its share of the row sum l.
+// 32-bit words a lane hands over for one partial unit: its O^T accumulators divided by the
+// unit's row sum, as f16 pairs (a weighted mean of V rows, so within V's f16 range), then the
+// running offset m and the row sum l of the piece's keys (fp32).
 template <int D>
-constexpr int partial_floats() { return 16 * (D / 32) + 2; }
+constexpr int partial_words() { return 8 * (D / 32) + 2; }
 
 // Integer min / max of 64-bit values (in device code the generic min / max of int64_t go through
 // double precision).
@@ -602,15 +603,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     }
 
     if constexpr (SK) {
-        if (part_slot >= 0) {  // split unit: hand over O, m, l (merged by attn_merge_kernel)
-            constexpr int NV = partial_floats<D>();
-            float* dst = p.ws + ((int64_t)part_slot * NW + wave) * NV * 64 + lane;
+        if (part_slot >= 0) {  // split unit: hand over O / l, m, l (merged by attn_merge_kernel)
+            constexpr int NV = partial_words<D>();
+            uint32_t* dst = reinterpret_cast<uint32_t*>(p.ws) + ((int64_t)part_slot * NW + wave) * NV * 64 + lane;
+            const float lt = half_swap_sum(l_run);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(16 * db + r) * 64] = o[db][r];
-            dst[16 * DB * 64] = m_run;
-            dst[(16 * DB + 1) * 64] = l_run;
+                for (int i = 0; i < 8; ++i) dst[(8 * db + i) * 64] = pack_f16x2(o[db][2 * i] * inv, o[db][2 * i + 1] * inv);
+            dst[8 * DB * 64] = __float_as_uint(m_run);
+            dst[(8 * DB + 1) * 64] = __float_as_uint(lt);
             return;
         }
     }
@@ -672,7 +675,7 @@ template <int D, int DT, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     constexpr bool OUT_BF16 = DT != kDtF16;
     constexpr int DB = D / 32;
-    constexpr int NV = partial_floats<D>();
+    constexpr int NV = partial_words<D>();
     constexpr int kBM = NW * 32;
     const int e = blockIdx.x / DB, db = blockIdx.x % DB;
     const int nT = p.sk_tiles, P = p.sk_wgs;
@@ -687,9 +690,9 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     const int rem0 = (int)(p.sk_work * w0 % P);
     const int64_t step_q = p.sk_work / P;
     const int step_r = (int)(p.sk_work % P);
-    const float* base = p.ws + (int64_t)wave * NV * 64 + lane;
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(p.ws) + (int64_t)wave * NV * 64 + lane;
     constexpr int64_t kSlot = (int64_t)NW * NV * 64;
-    const float* first = base + (beg0 >= lo ? 2 * w0 : 2 * w0 + 1) * kSlot;
+    const uint32_t* first = base + (beg0 >= lo ? 2 * w0 : 2 * w0 + 1) * kSlot;
     // the pieces of workgroups w0, w0 + 1, ... that start before hi, stepping
     // w_begin(w + 1) = w_begin(w) + step_q (+1 when the remainder of sk_work * w wraps)
     auto next = [&](int64_t& beg, int& rem) __attribute__((always_inline)) {
@@ -720,26 +723,30 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
         }
     };
     float M = -1e30f;
-    each_piece([&](const float* src, bool ne) {
-        const float mv = src[16 * DB * 64];
+    each_piece([&](const uint32_t* src, bool ne) {
+        const float mv = __uint_as_float(src[8 * DB * 64]);
         M = fmaxf(M, ne ? mv : -1e30f);
     });
     float l = 0.f;
     float o[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    each_piece([&](const float* src, bool ne) {
-        const float mv = src[16 * DB * 64], lv = src[(16 * DB + 1) * 64];
-        float ov[16];
+    // piece i holds O_i / l_i: the output is sum_i w_i (O_i / l_i) / sum_i w_i, w_i = l_i 2^(m_i - M)
+    each_piece([&](const uint32_t* src, bool ne) {
+        const float mv = __uint_as_float(src[8 * DB * 64]), lv = __uint_as_float(src[(8 * DB + 1) * 64]);
+        uint32_t ow[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ov[r] = src[(16 * db + r) * 64];
-        const float f = ne ? __builtin_amdgcn_exp2f(mv - M) : 0.f;
-        l += lv * f;
+        for (int i = 0; i < 8; ++i) ow[i] = src[(8 * db + i) * 64];
+        const float f = ne ? lv * __builtin_amdgcn_exp2f(mv - M) : 0.f;
+        l += f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] += ov[r] * f;
+        for (int i = 0; i < 8; ++i) {
+            const f16x2 h = __builtin_bit_cast(f16x2, ow[i]);
+            o[2 * i] += (float)h[0] * f;
+            o[2 * i + 1] += (float)h[1] * f;
+        }
     });
-    const float lt = half_swap_sum(l);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float inv = l > 0.f ? 1.f / l : 0.f;  // l is already the whole row's weight
     const int u = p.sk_full * p.sk_wgs + e;
     const int qblk = u % p.n_qblk, bh = u / p.n_qblk, h = bh % p.Hq, b = bh / p.Hq;
     const int qrow = qblk * kBM + wave * 32 + j;
@@ -766,7 +773,7 @@ constexpr int kBalancedWaves = 8;
 
 // Workspace of a balanced launch: two partial slots per workgroup, one per wave and lane.
 int64_t balanced_workspace_bytes(int d, int wgs) {
-    return (int64_t)2 * wgs * kBalancedWaves * 64 * (16 * (d / 32) + 2) * (int64_t)sizeof(float);
+    return (int64_t)2 * wgs * kBalancedWaves * 64 * (8 * (d / 32) + 2) * (int64_t)sizeof(uint32_t);
 }
 
 // A balanced launch pays when the grid's rounds would keep the slots under 90 % busy, for
