@@ -34,7 +34,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before the timed ones (default: at least 5 and at least 100 ms of GPU work, "
+                        "so the GPU reaches its steady clock; the count run is reported)")
     p.add_argument("--workload", default="mha_20480_bf16")
     p.add_argument("--no-workspace", action="store_true",
                    help="streaming / cross workloads: plain attention launch instead of the balanced one")
@@ -242,10 +244,26 @@ def workload_flops(w) -> float:
     return 4.0 * w.B * w.Hq * w.d * float(visible_keys(w, np.arange(w.Lq)).sum())
 
 
+def warm_up(fn, warmup):
+    """Runs `warmup` untimed steps; with None, at least 5 steps and at least 100 ms of GPU work
+    (short steps need many to bring the GPU to its steady clock). Returns the count run."""
+    import torch
+    if warmup is not None:
+        for _ in range(warmup):
+            fn()
+        return warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 5 or time.perf_counter() - t0 < 0.1:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()  # the host must not run far ahead of the GPU
+    return n
+
+
 def time_loop(fn, steps, warmup):
     import torch
-    for _ in range(warmup):
-        fn()
+    warm_up(fn, warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -317,7 +335,8 @@ def main():
         gbs = (info["bytes_read"] + info["bytes_written"]) / (ms * 1e-3) / 1e9
         print(json.dumps({"workload": info["workload"], "ms": round(ms, 4), "GB/s": round(gbs, 1), **info}))
         return
-    ms_step, wall_ms = time_loop(step, args.steps, args.warmup)
+    args.warmup = warm_up(step, args.warmup)  # the steps' own warm-up; the count goes into the JSON line
+    ms_step, wall_ms = time_loop(step, args.steps, 0)
     ms_kern, _ = time_loop(kern, args.steps, 2) if kern is not step else (ms_step, wall_ms)
 
     hbm = {}
