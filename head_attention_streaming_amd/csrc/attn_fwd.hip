@@ -426,6 +426,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // barrier closing each step orders those writes before the next step's reads.
     auto step = [&](auto do_qk, auto do_pv, auto do_mask, int t, f32x16 (&sc)[KB], f32x16 (&sp)[KB]) __attribute__((always_inline)) {
         constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value, MASK = decltype(do_mask)::value;
+        // This wave's S = K Q^T products issue ahead of the other wave's softmax work on the SIMD:
+        // raised issue priority until they are queued (measured +0.3 to +4 % across launch shapes).
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (QK) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -444,6 +447,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (PV) {
             // P(t-1) as f16 operands; the row sum adds the f16 values the product uses
             const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
