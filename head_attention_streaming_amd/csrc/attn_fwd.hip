@@ -726,29 +726,30 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
             beg = nb;
         }
     };
-    float M = -1e30f;
-    each_piece([&](const uint32_t* src, bool ne) {
-        const float mv = __uint_as_float(src[8 * DB * 64]);
-        M = fmaxf(M, ne ? mv : -1e30f);
-    });
-    float l = 0.f;
+    // one pass in key order with a running maximum: piece i holds O_i / l_i, so the output is
+    // sum_i w_i (O_i / l_i) / sum_i w_i with w_i = l_i 2^(m_i - M); the loads of every piece are
+    // independent of the running state, so several pieces' loads are in flight together
+    float M = -1e30f, l = 0.f;
     float o[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    // piece i holds O_i / l_i: the output is sum_i w_i (O_i / l_i) / sum_i w_i, w_i = l_i 2^(m_i - M)
     each_piece([&](const uint32_t* src, bool ne) {
         const float mv = __uint_as_float(src[8 * DB * 64]), lv = __uint_as_float(src[(8 * DB + 1) * 64]);
         uint32_t ow[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) ow[i] = src[(8 * db + i) * 64];
-        const float f = ne ? lv * __builtin_amdgcn_exp2f(mv - M) : 0.f;
-        l += f;
+        const float mi = ne ? mv : -1e30f;
+        const float mn = fmaxf(M, mi);
+        const float a = __builtin_amdgcn_exp2f(M - mn);
+        const float f = ne ? lv * __builtin_amdgcn_exp2f(mi - mn) : 0.f;
+        l = l * a + f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const f16x2 h = __builtin_bit_cast(f16x2, ow[i]);
-            o[2 * i] += (float)h[0] * f;
-            o[2 * i + 1] += (float)h[1] * f;
+            o[2 * i] = o[2 * i] * a + (float)h[0] * f;
+            o[2 * i + 1] = o[2 * i + 1] * a + (float)h[1] * f;
         }
+        M = mn;
     });
     const float inv = l > 0.f ? 1.f / l : 0.f;  // l is already the whole row's weight
     const int u = p.sk_full * p.sk_wgs + e;
