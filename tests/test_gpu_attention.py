@@ -222,24 +222,43 @@ def test_f16_v_with_bf16_qk_equals_bf16_path(causal, Lk):
     assert_attention_close(a, ref, "f16 v")
 
 
-def test_kv_region_past_4gib_uses_rebased_resources():
-    """K/V regions whose rows (up to one tile past Lk) span 4 GiB or more: 64 K/V heads x 262200
-    keys x 128 features of bf16 = 4.3 GB per tensor. Every head's rows are read through 32-bit
-    buffer offsets from a base that moves with the tile; three heads are checked against the
+BIG_CASES = [
+    # name, Lk, dtype, causal: 64 K/V heads x d=128; rows up to one tile past Lk span
+    # (Lk + 64) * 64 * 128 * elem bytes; 4 GiB or more takes per-tile resources
+    ("big_bf16", 262200, "bf16", False),
+    ("big_bf16_causal", 262200, "bf16", True),
+    ("big_fp8", 524400, "e4m3", False),
+    ("limit_bf16_just_under_4gib", 262079, "bf16", False),   # the largest Lk on one resource
+]
+
+
+@pytest.mark.parametrize("case", BIG_CASES, ids=[c[0] for c in BIG_CASES])
+def test_kv_regions_at_and_past_4gib(case):
+    """K/V regions whose rows reach 4 GiB (4.3 GB tensors): every head's rows are read through
+    32-bit buffer offsets, from a base that moves with the tile past the limit; just under it,
+    from one resource with offsets up to the last tile. Three heads are checked against the
     oracle on their own slices (all 40 query rows, every key, ragged last tile)."""
-    B, Lq, Lk, H, d = 1, 40, 262200, 64, 128
-    assert (Lk + 64) * H * d * 2 > 0xFFFFFFFF
-    print(f"[case] big region B={B} Lq={Lq} Lk={Lk} H={H} d={d} bf16", flush=True)
+    name, Lk, dt, causal = case
+    B, Lq, H, d = 1, 40, 64, 128
+    elem = 1 if dt == "e4m3" else 2
+    big = (Lk + 64) * H * d * elem > 0xFFFFFFFF
+    assert big == name.startswith("big"), name
+    print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} H={H} d={d} {dt} causal={causal}", flush=True)
     g = torch.Generator(device=DEV).manual_seed(4242)
-    q = torch.randn((B, Lq, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
-    k = torch.randn((B, Lk, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
-    v = torch.randn((B, Lk, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
-    out = torch.empty_like(q)
-    binding.attn_forward(q, k, v, out, d ** -0.5, False)
+    def draw(L):
+        x = torch.randn((B, L, H, d), generator=g, device=DEV, dtype=torch.bfloat16)
+        return x.to(torch.float8_e4m3fn) if dt == "e4m3" else x
+    q, k, v = draw(Lq), draw(Lk), draw(Lk)
+    out = torch.empty((B, Lq, H, d), dtype=torch.bfloat16, device=DEV)
+    if dt == "e4m3":
+        binding.attn_forward_fp8(q, k, v, out, d ** -0.5, causal=causal)
+    else:
+        binding.attn_forward(q, k, v, out, d ** -0.5, causal)
     torch.cuda.synchronize()
     for h in (0, 37, 63):
         qh, kh, vh = (t[:, :, h:h + 1].contiguous().cpu() for t in (q, k, v))
         ref = oracle.attention(widen(qh).reshape(qh.shape), widen(kh).reshape(kh.shape),
-                               widen(vh).reshape(vh.shape), d ** -0.5)
-        assert_attention_close(out[:, :, h:h + 1].contiguous(), ref, f"big region head {h}")
-    del k, v
+                               widen(vh).reshape(vh.shape), d ** -0.5, causal)
+        assert_attention_close(out[:, :, h:h + 1].contiguous(), ref, f"{name} head {h}")
+    del q, k, v, out
+    torch.cuda.empty_cache()
