@@ -888,7 +888,13 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // +6-8 %, 8192 keys -7 %.
     const bool banded = a.win_right >= 0 && (a.win_left >= 0 ? (int64_t)a.win_left + a.win_right <= 2048 : a.Lk <= 4096);
     if (banded && wg256 >= 2 * cus) return launch<D, DT, 4, 1>(a, stream);
-    if (wg256 >= 4 * cus) return launch<D, DT, 8, 1>(a, stream);
+    // 256-row workgroups for four or more blocks per CU, or for one or more per CU whose rounds
+    // keep the CUs at least 90 % busy over key loops of at least 2048 keys. Measured: one or two
+    // full rounds +12-14 % (64 heads x 2048 x 7140 keys, [1,4096,16,128], causal
+    // [2,2048,16,128]); 1.25-2.25 rounds lose 2-6 % (one slot per CU quantises coarser than two
+    // 128-row slots) and loops of 512-1024 keys 9 %, so those keep 128-row blocks.
+    const bool full8 = wg256 >= cus && wg256 * 10 >= (wg256 + cus - 1) / cus * cus * 9;
+    if (wg256 >= 4 * cus || (full8 && a.Lk >= 2048)) return launch<D, DT, 8, 1>(a, stream);
     const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
     if (wg128 <= cus && a.Lk >= 512) return launch<D, DT, 8, 2>(a, stream);
     return launch<D, DT, 4, 1>(a, stream);
