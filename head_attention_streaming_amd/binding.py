@@ -19,7 +19,7 @@ SA_ERR_UNSUPPORTED_CODE = -3
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
 
-EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
+EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "qk_norm_rope_v", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
            "kv_cache_append_ex", "kv_cache_rope", "attn_forward", "attn_forward_f16", "attn_forward_kvstride",
            "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "attn_forward_qnorm",
            "sa_last_error")
@@ -51,6 +51,7 @@ def lib():
         L.kv_cache_append.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, P]
         L.kv_cache_append_ex.argtypes = [P, P, P, P, I, I, I, I, I, I, I64, I, I, P]
         L.qk_norm_rope_ex.argtypes = [P, P, I64, P, P, I64, P, P, P, I, I, I, I, I, F, I, I, I, P]
+        L.qk_norm_rope_v.argtypes = [P, P, I64, P, P, I64, P, P, I64, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
         L.kv_cache_positions.argtypes = [I64, I, I, I, ctypes.POINTER(I64), I]
         L.kv_cache_rope.argtypes = [P, P, P, I, I, I, I, I, I, I64, I, P]
         L.attn_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P]
@@ -59,7 +60,7 @@ def lib():
         L.attn_forward_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
         L.attn_forward_workspace_bytes.argtypes = [I]
         L.attn_forward_ws.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
-        L.attn_forward_qnorm.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
+        L.attn_forward_qnorm.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
         L.sa_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = I
@@ -158,16 +159,19 @@ def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None
 
 
 def attn_forward_qnorm(q, k, v, out, scale: float, gamma_q, eps: float = 1e-6, workspace=None, Lk: int | None = None,
-                       window=(-1, -1)):
-    """Attention whose query rows are RMS-normalised (head scope, weights gamma_q fp32 [d]) as
-    they are loaded; q itself is not modified. Same as qk_norm_rope (Q only, no RoPE) followed by
-    attn_forward_ws, without the normalised Q round trip through memory."""
+                       window=(-1, -1), rope_cs=None, rope_style: int = SA_ROPE_NONE):
+    """Attention whose query rows are RMS-normalised (head scope, weights gamma_q fp32 [d]) and,
+    with rope_cs (fp32 [Lq, d]: cos then sin per row, as qk_norm_rope_v writes) and rope_style
+    SA_ROPE_SPLIT / SA_ROPE_INTERLEAVED, rotated as they are loaded; q itself is not modified.
+    Same as qk_norm_rope on the queries followed by attn_forward_ws, without the normalised Q
+    round trip through memory."""
     B, Lq, Hq, d = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     left, right = (int(x) for x in window)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("attn_forward_qnorm",
-           lib().attn_forward_qnorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(gamma_q), float(eps), B, Hq, Hkv, Lq,
+           lib().attn_forward_qnorm(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(gamma_q), float(eps), _ptr(rope_cs),
+                                    int(rope_style) if rope_cs is not None else SA_ROPE_NONE, B, Hq, Hkv, Lq,
                                     S if Lk is None else int(Lk), d, float(scale), left, right, S * Hkv * d,
                                     _attn_dtype(q, k, v), _ptr(workspace), ws_bytes, _stream(q)))
     return out
@@ -209,6 +213,28 @@ def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None,
                                                     k_out_bstride, _ptr(gamma_q), _ptr(gamma_k), _ptr(angles), B, L,
                                                     Hq, Hkv, d, float(eps), norm_scope, rope_style, out_dtype,
                                                     _stream(q_in)))
+
+
+def qk_norm_rope_v(k_in, k_out, v_in, v_out, gamma_k=None, angles=None, eps: float = 1e-6,
+                   norm_scope: int = SA_NORM_HEAD, rope_style: int = SA_ROPE_SPLIT, rope_cs_out=None,
+                   k_out_bstride=None, v_out_bstride=None, q_in=None, q_out=None, gamma_q=None, q_out_bstride=None):
+    """The chunk prologue in one launch: keys normalised (and rotated unless rope_style has
+    SA_ROPE_AFTER_CACHE) into k_out, values copied into v_out (both may be cache row-range views:
+    pass the cache's batch strides), optional queries as in qk_norm_rope, and optionally the
+    chunk's cos/sin table (fp32 [L, d]) for attn_forward_qnorm. bf16 in; out type of k_out."""
+    B, L, Hkv, d = (k_in if k_in is not None else v_in).shape
+    Hq = q_in.shape[2] if q_in is not None else 0
+    if k_out_bstride is None:
+        k_out_bstride = L * Hkv * d
+    if v_out_bstride is None:
+        v_out_bstride = L * Hkv * d
+    if q_out_bstride is None:
+        q_out_bstride = L * max(Hq, 1) * d
+    out_dtype = _dtype_code(k_out if k_out is not None else v_out)
+    _check("qk_norm_rope_v", lib().qk_norm_rope_v(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
+                                                  k_out_bstride, _ptr(v_in), _ptr(v_out), v_out_bstride, _ptr(gamma_q),
+                                                  _ptr(gamma_k), _ptr(angles), _ptr(rope_cs_out), B, L, Hq, Hkv, d,
+                                                  float(eps), norm_scope, rope_style, out_dtype, _stream(k_in)))
 
 
 def kv_cache_slot(chunk_idx: int, chunk_len: int, sink_size: int, window_size: int):
@@ -274,6 +300,8 @@ class BlockKVCache:
         self.v = torch.empty((B, S, Hkv, d), dtype=v_dtype or dtype, device=device)
         # after-cache RoPE: the cache keeps unrotated keys; each step rotates the visible ones here
         self.k_rot = torch.empty_like(self.k) if after_cache_rope else None
+        # the chunk's RoPE cos/sin table [Lc, d] for queries rotated inside the attention
+        self.rope_cs = torch.empty((chunk_len, d), dtype=torch.float32, device=device)
         self.slot_base = 0
         self.visible_len = 0
         self._current = None
@@ -302,21 +330,27 @@ class BlockKVCache:
 
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
-                               rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None):
+                               rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None,
+                               fuse: bool = True):
     """One streaming self-attention chunk as library calls between before_update / after_update.
 
+    Fused route (default, for a bf16 cache with bf16 values and head-scope norm): qk_norm_rope_v
+    writes the normalised (rotated, unless after-cache RoPE) keys and the values into the
+    chunk's cache slot and the chunk's cos/sin table into cache.rope_cs in one launch; the
+    attention (attn_forward_qnorm) normalises and rotates the raw queries as it loads them, so
+    q_buf is not used. Other caches and fuse=False take the separate route:
+    qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot) -> kv_cache_append
+    (v_in -> cache values) -> attention over the visible cache.
     A cache of float8_e4m3fn (BlockKVCache(dtype=torch.float8_e4m3fn), before-cache RoPE only) with
     an E4M3 q_buf is the FP8 path: the prologue rounds Q and K to E4M3, the append rounds V, and
     attention runs on the FP8 MFMA with a bf16 out.
-    Before-cache RoPE (cache.k_rot is None): angles [Lc, d/2] for the chunk's positions;
-    qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot, both rotated) ->
-    kv_cache_append (v_in -> cache values) -> attn_forward_kvstride over the visible cache.
+    Before-cache RoPE (cache.k_rot is None): angles [Lc, d/2] for the chunk's positions.
     After-cache RoPE (cache built with after_cache_rope=True): angles [visible_len, d/2] by
-    logical row; qk_norm_rope rotates q_in with the chunk's rows (the last Lc) and stores the
-    normalised keys unrotated -> kv_cache_append -> kv_cache_rope (visible keys -> cache.k_rot)
-    -> attn_forward_kvstride over cache.k_rot and the cached values.
+    logical row; the queries are rotated with the chunk's rows (the last Lc) and the keys are
+    stored unrotated; kv_cache_rope then rotates the visible keys into cache.k_rot, which the
+    attention reads.
     workspace (attn_workspace): lets the attention run balanced when its grid would leave CU
-    slots idle (attn_forward_ws). Returns the visible length used.
+    slots idle. Returns the visible length used.
     """
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
@@ -325,16 +359,28 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
         raise StreamAttnError("stream_self_attention_step", SA_ERR_UNSUPPORTED_CODE,
                               "after-cache RoPE is built for a bf16 cache only")
     q_angles = angles[visible - cache.chunk_len:visible] if after else angles
-    qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
-                 norm_scope, rope_style | (SA_ROPE_AFTER_CACHE if after else 0),
-                 k_out_bstride=S * cache.Hkv * cache.d)
-    kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
+    flag = SA_ROPE_AFTER_CACHE if after else 0
+    fused = (fuse and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
+             cache.v.dtype == torch.bfloat16 and q_in.dtype == torch.bfloat16)
+    if fused:
+        rope = rope_style != SA_ROPE_NONE
+        qk_norm_rope_v(k_in, cache.k[:, slot:], v_in, cache.v[:, slot:], gamma_k, q_angles if rope else None, eps,
+                       norm_scope, (rope_style | flag) if rope else SA_ROPE_NONE,
+                       rope_cs_out=cache.rope_cs if rope else None, k_out_bstride=S * cache.Hkv * cache.d,
+                       v_out_bstride=S * cache.Hkv * cache.d)
+    else:
+        qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
+                     norm_scope, rope_style | flag, k_out_bstride=S * cache.Hkv * cache.d)
+        kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
     keys = cache.k
     if after:
         kv_cache_rope(cache.k, cache.k_rot, angles, chunk_idx, cache.chunk_len, cache.sink_size, cache.window_size,
                       rope_style)
         keys = cache.k_rot
-    if workspace is not None:
+    if fused:
+        attn_forward_qnorm(q_in, keys, cache.v, out, scale, gamma_q, eps, workspace=workspace, Lk=visible,
+                           rope_cs=cache.rope_cs if rope_style != SA_ROPE_NONE else None, rope_style=rope_style)
+    elif workspace is not None:
         attn_forward_ws(q_buf, keys, cache.v, out, scale, workspace, Lk=visible)
     else:
         attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)

@@ -69,6 +69,10 @@ struct KParams {
     // (null: queries are used as given) and epsilon.
     const float* gamma_q;
     float q_eps;
+    // Optional RoPE of the normalised query rows: table [Lq, D] fp32 (row i: cos then sin of
+    // query row i's angles), pairing 1 split (r, r + D/2) or 2 interleaved (2r, 2r + 1).
+    const float* q_cs;
+    int q_rope;
 };
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
@@ -317,12 +321,46 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 const f32x4* gp = reinterpret_cast<const f32x4*>(p.gamma_q + 16 * cc + 8 * g);
                 const f32x4 g0 = gp[0], g1 = gp[1];
                 const float gw[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[cc][e] = gw[e] * (z[cc][e] * r);
+            }
+            if (p.q_cs) {  // uniform. RoPE of the normalised row; both features of a pair are in this lane
+                const float* cs_row = p.q_cs + (int64_t)min(qrow, p.Lq - 1) * D;
+                if (p.q_rope == 1) {  // split pairs (r, r + D/2): feature 16c + 8g + e of chunks c, c + DC/2
+#pragma unroll
+                    for (int cc = 0; cc < DC / 2; ++cc) {
+                        const f32x4* cp = reinterpret_cast<const f32x4*>(cs_row + 16 * cc + 8 * g);
+                        const f32x4* sp = reinterpret_cast<const f32x4*>(cs_row + D / 2 + 16 * cc + 8 * g);
+                        const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+                        const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float a0 = z[cc][e], b0 = z[cc + DC / 2][e];
+                            z[cc][e] = cv[e] * a0 - sv[e] * b0;
+                            z[cc + DC / 2][e] = sv[e] * a0 + cv[e] * b0;
+                        }
+                    }
+                } else {  // interleaved pairs (2r, 2r + 1): r = 8c + 4g + e for e < 4
+#pragma unroll
+                    for (int cc = 0; cc < DC; ++cc) {
+                        const f32x4 cv = *reinterpret_cast<const f32x4*>(cs_row + 8 * cc + 4 * g);
+                        const f32x4 sv = *reinterpret_cast<const f32x4*>(cs_row + D / 2 + 8 * cc + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float a0 = z[cc][2 * e], b0 = z[cc][2 * e + 1];
+                            z[cc][2 * e] = cv[e] * a0 - sv[e] * b0;
+                            z[cc][2 * e + 1] = sv[e] * a0 + cv[e] * b0;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) {
                 uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x0 = gw[2 * i] * (z[cc][2 * i] * r), x1 = gw[2 * i + 1] * (z[cc][2 * i + 1] * r);
-                    w[i] = BF16 ? pack_bf16x2(x0, x1) : pack_f16x2(x0, x1);
-                }
+                for (int i = 0; i < 4; ++i)
+                    w[i] = BF16 ? pack_bf16x2(z[cc][2 * i], z[cc][2 * i + 1]) : pack_f16x2(z[cc][2 * i], z[cc][2 * i + 1]);
                 qf[cc] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
@@ -827,6 +865,8 @@ KParams make_params(const AttnArgs& a) {
     p.c = a.scale * kLog2e;
     p.gamma_q = a.gamma_q;
     p.q_eps = a.q_eps;
+    p.q_cs = a.q_cs;
+    p.q_rope = a.q_rope;
     p.nblocks = (int)((int64_t)p.n_qblk * a.Hq * a.B);
     return p;
 }

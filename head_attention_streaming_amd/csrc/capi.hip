@@ -84,7 +84,7 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
 int run_attn(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq, int Lk, int d,
              float scale, int win_left, int win_right, int64_t kv_bstride, int dtype, void* stream,
              void* workspace = nullptr, int64_t workspace_bytes = 0, const float* gamma_q = nullptr,
-             float q_eps = 0.f) {
+             float q_eps = 0.f, const float* q_cs = nullptr, int q_rope = 0) {
     const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, kv_bstride, dtype);
     if (st < 0) return st;
     if (st > 0) return ok();
@@ -113,6 +113,8 @@ int run_attn(const void* q, const void* k, const void* v, void* out, int B, int 
     a.dtype = dtype;
     a.gamma_q = gamma_q;
     a.q_eps = q_eps;
+    a.q_cs = q_cs;
+    a.q_rope = q_rope;
     return hip_status(sa::launch_attn_fwd(a, static_cast<hipStream_t>(stream)), "attn_forward launch");
 }
 
@@ -160,15 +162,21 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out, int 
 }
 
 int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, const float* gamma_q, float eps,
-                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale, int window_left, int window_right,
-                       int64_t kv_bstride, int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+                       const float* rope_cs, int rope_style, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                       float scale, int window_left, int window_right, int64_t kv_bstride, int dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
     if (!gamma_q) return fail(SA_ERR_NULL, "attn_forward_qnorm: gamma_q is null");
     if (!aligned16(gamma_q)) return fail(SA_ERR_ALIGN, "attn_forward_qnorm: gamma_q must be 16-byte aligned");
     if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "attn_forward_qnorm: eps must be >= 0 and finite");
     if (dtype == SA_DTYPE_FP8_E4M3)
         return fail(SA_ERR_UNSUPPORTED, "attn_forward_qnorm: the fused query norm takes 16-bit queries");
+    if (rope_style != SA_ROPE_NONE && rope_style != SA_ROPE_SPLIT && rope_style != SA_ROPE_INTERLEAVED)
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward_qnorm: unknown RoPE pairing %d", rope_style);
+    if ((rope_style != SA_ROPE_NONE) != (rope_cs != nullptr))
+        return fail(SA_ERR_NULL, "attn_forward_qnorm: the cos/sin table must be given iff RoPE is enabled");
+    if (rope_cs && !aligned16(rope_cs)) return fail(SA_ERR_ALIGN, "attn_forward_qnorm: rope_cs must be 16-byte aligned");
     return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype, stream,
-                    workspace, workspace_bytes, gamma_q, eps);
+                    workspace, workspace_bytes, gamma_q, eps, rope_cs, rope_style);
 }
 
 int attn_forward_window(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
@@ -252,13 +260,13 @@ int kv_cache_append(const void* k_new, const void* v_new, void* cache_k, void* c
                               SA_DTYPE_BF16, SA_DTYPE_BF16, stream);
 }
 
-int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
-                    int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
-                    int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, int out_dtype,
-                    void* stream) {
+int qk_norm_rope_v(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
+                   int64_t k_out_bstride, const void* v_in, void* v_out, int64_t v_out_bstride, const float* gamma_q,
+                   const float* gamma_k, const float* rope_angles, float* rope_cs_out, int B, int L, int Hq, int Hkv,
+                   int d, float eps, int norm_scope, int rope_style, int out_dtype, void* stream) {
     if (out_dtype != SA_DTYPE_BF16 && out_dtype != SA_DTYPE_FP8_E4M3)
         return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: output dtype %d is not bf16 (0) or fp8 e4m3 (2)", out_dtype);
-    if (B < 0 || L < 0 || Hq <= 0 || (k_in && Hkv <= 0))
+    if (B < 0 || L < 0 || (q_in && Hq <= 0) || ((k_in || v_in) && Hkv <= 0))
         return fail(SA_ERR_RANGE, "qk_norm_rope: negative or zero size");
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: head dim %d not built (64, 128)", d);
     if (norm_scope != SA_NORM_NONE && norm_scope != SA_NORM_HEAD && norm_scope != SA_NORM_INNER)
@@ -267,43 +275,55 @@ int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride, const 
     if ((rope_style & ~(SA_ROPE_AFTER_CACHE | 3)) || pairing > SA_ROPE_INTERLEAVED ||
         (rope_style == SA_ROPE_AFTER_CACHE))
         return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: unknown RoPE style %d", rope_style);
-    if (norm_scope == SA_NORM_INNER && k_in && Hkv != Hq)
+    if (norm_scope == SA_NORM_INNER && q_in && k_in && Hkv != Hq)
         return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: inner-scope norm needs Hq == Hkv (grouped heads use head scope)");
     if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "qk_norm_rope: eps must be >= 0 and finite");
     if (B == 0 || L == 0) return ok();
-    if (!q_in || !q_out) return fail(SA_ERR_NULL, "qk_norm_rope: null q pointer");
+    if ((q_in == nullptr) != (q_out == nullptr)) return fail(SA_ERR_NULL, "qk_norm_rope: q_in and q_out must both be set or both NULL");
     if ((k_in == nullptr) != (k_out == nullptr)) return fail(SA_ERR_NULL, "qk_norm_rope: k_in and k_out must both be set or both NULL");
-    if (norm_scope != SA_NORM_NONE && (!gamma_q || (k_in && !gamma_k)))
+    if ((v_in == nullptr) != (v_out == nullptr)) return fail(SA_ERR_NULL, "qk_norm_rope: v_in and v_out must both be set or both NULL");
+    if (!q_in && !k_in && !v_in) return fail(SA_ERR_NULL, "qk_norm_rope: no input rows");
+    if (norm_scope != SA_NORM_NONE && ((q_in && !gamma_q) || (k_in && !gamma_k)))
         return fail(SA_ERR_NULL, "qk_norm_rope: RMSNorm weights required");
-    if (norm_scope == SA_NORM_NONE && (gamma_q || gamma_k))
-        return fail(SA_ERR_SHAPE, "qk_norm_rope: weights given with norm scope none");
+    if ((norm_scope == SA_NORM_NONE && (gamma_q || gamma_k)) || (!q_in && gamma_q) || (!k_in && gamma_k))
+        return fail(SA_ERR_SHAPE, "qk_norm_rope: weights given for rows that are not normalised");
     if ((pairing != SA_ROPE_NONE) != (rope_angles != nullptr))
         return fail(SA_ERR_NULL, "qk_norm_rope: angles must be given iff RoPE is enabled");
-    for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out, (const void*)gamma_q,
-                          (const void*)gamma_k})
+    if (rope_cs_out && pairing == SA_ROPE_NONE)
+        return fail(SA_ERR_SHAPE, "qk_norm_rope: a cos/sin table needs RoPE angles");
+    for (const void* p : {q_in, (const void*)q_out, k_in, (const void*)k_out, v_in, (const void*)v_out,
+                          (const void*)gamma_q, (const void*)gamma_k, (const void*)rope_cs_out})
         if (p && !aligned16(p)) return fail(SA_ERR_ALIGN, "qk_norm_rope: pointers must be 16-byte aligned");
-    const int64_t nq = mul4(1, L, Hq, d);
-    if (nq < 0 || mul4(B, L, k_in ? Hkv : 1, d) < 0) return fail(SA_ERR_RANGE, "qk_norm_rope: tensor too large");
+    const int64_t nq = mul4(1, L, q_in ? Hq : 1, d);
+    const int64_t nkv = mul4(1, L, (k_in || v_in) ? Hkv : 1, d);
+    if (nq < 0 || nkv < 0 || mul4(B, L, (k_in || v_in) ? Hkv : 1, d) < 0 || mul4(B, L, q_in ? Hq : 1, d) < 0)
+        return fail(SA_ERR_RANGE, "qk_norm_rope: tensor too large");
     const int align_elems = out_dtype == SA_DTYPE_FP8_E4M3 ? 16 : 8;  // 16-byte aligned batch strides
-    if (q_out_bstride < nq || q_out_bstride % align_elems) return fail(SA_ERR_SHAPE, "qk_norm_rope: bad q_out_bstride");
-    if (k_in && (k_out_bstride < (int64_t)L * Hkv * d || k_out_bstride % align_elems))
+    if (q_in && (q_out_bstride < nq || q_out_bstride % align_elems)) return fail(SA_ERR_SHAPE, "qk_norm_rope: bad q_out_bstride");
+    if (k_in && (k_out_bstride < nkv || k_out_bstride % align_elems))
         return fail(SA_ERR_SHAPE, "qk_norm_rope: bad k_out_bstride");
+    if (v_in && (v_out_bstride < nkv || v_out_bstride % align_elems))
+        return fail(SA_ERR_SHAPE, "qk_norm_rope: bad v_out_bstride");
     if ((int64_t)B * L > INT32_MAX) return fail(SA_ERR_RANGE, "qk_norm_rope: grid too large");
     sa::NormRopeArgs a{};
     a.q_in = q_in;
-    a.q_in_bstride = nq;
+    a.q_in_bstride = q_in ? nq : 0;
     a.q_out = q_out;
     a.q_out_bstride = q_out_bstride;
     a.k_in = k_in;
     a.k_out = k_out;
     a.k_out_bstride = k_out_bstride;
+    a.v_in = v_in;
+    a.v_out = v_out;
+    a.v_out_bstride = v_out_bstride;
+    a.cs_out = rope_cs_out;
     a.gamma_q = gamma_q;
     a.gamma_k = gamma_k;
     a.angles = rope_angles;
     a.B = B;
     a.L = L;
-    a.Hq = Hq;
-    a.Hkv = k_in ? Hkv : 0;
+    a.Hq = q_in ? Hq : 0;
+    a.Hkv = (k_in || v_in) ? Hkv : 0;
     a.d = d;
     a.eps = eps;
     a.norm_scope = norm_scope;
@@ -311,6 +331,22 @@ int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride, const 
     a.rope_keys = (rope_style & SA_ROPE_AFTER_CACHE) ? 0 : 1;
     a.out_fp8 = out_dtype == SA_DTYPE_FP8_E4M3;
     return hip_status(sa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream)), "qk_norm_rope launch");
+}
+
+int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,
+                    int64_t k_out_bstride, const float* gamma_q, const float* gamma_k, const float* rope_angles, int B,
+                    int L, int Hq, int Hkv, int d, float eps, int norm_scope, int rope_style, int out_dtype,
+                    void* stream) {
+    if (out_dtype != SA_DTYPE_BF16 && out_dtype != SA_DTYPE_FP8_E4M3)
+        return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: output dtype %d is not bf16 (0) or fp8 e4m3 (2)", out_dtype);
+    if (B < 0 || L < 0 || Hq <= 0 || (k_in && Hkv <= 0))
+        return fail(SA_ERR_RANGE, "qk_norm_rope: negative or zero size");
+    if (B > 0 && L > 0 && (!q_in || !q_out)) {
+        if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "qk_norm_rope: head dim %d not built (64, 128)", d);
+        return fail(SA_ERR_NULL, "qk_norm_rope: null q pointer");
+    }
+    return qk_norm_rope_v(q_in, q_out, q_out_bstride, k_in, k_out, k_out_bstride, nullptr, nullptr, 0, gamma_q, gamma_k,
+                          rope_angles, nullptr, B, L, Hq, Hkv, d, eps, norm_scope, rope_style, out_dtype, stream);
 }
 
 int qk_norm_rope(const void* q_in, void* q_out, int64_t q_out_bstride, const void* k_in, void* k_out,

@@ -102,11 +102,15 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     const int rs = tid / LPR;             // row slot within a pass
     const int f0 = 8 * li;
 
-    const int rows = a.Hq + (a.k_in ? a.Hkv : 0);
-    const uint16_t* qin = static_cast<const uint16_t*>(a.q_in) + b * a.q_in_bstride + (int64_t)p * a.Hq * D;
+    // rows of the token: Hq query rows, then Hkv key rows (if k_in), then Hkv value rows (if v_in)
+    const int nk = a.k_in ? a.Hkv : 0;
+    const int rows = a.Hq + nk + (a.v_in ? a.Hkv : 0);
+    const uint16_t* qin = a.q_in ? static_cast<const uint16_t*>(a.q_in) + b * a.q_in_bstride + (int64_t)p * a.Hq * D : nullptr;
     const uint16_t* kin = a.k_in ? static_cast<const uint16_t*>(a.k_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
-    Out* qout = static_cast<Out*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D;
+    const uint16_t* vin = a.v_in ? static_cast<const uint16_t*>(a.v_in) + ((int64_t)b * a.L + p) * a.Hkv * D : nullptr;
+    Out* qout = a.q_out ? static_cast<Out*>(a.q_out) + b * a.q_out_bstride + (int64_t)p * a.Hq * D : nullptr;
     Out* kout = a.k_out ? static_cast<Out*>(a.k_out) + b * a.k_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
+    Out* vout = a.v_out ? static_cast<Out*>(a.v_out) + b * a.v_out_bstride + (int64_t)p * a.Hkv * D : nullptr;
 
     // Rows are handled NB passes at a time: all NB loads are issued before any is used, so each
     // thread keeps NB 16-byte reads in flight. rows_padded keeps every lane of a row group in
@@ -120,7 +124,9 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
             const int row = base + rs + nb * RPP;
             raw[nb] = u32x4{0u, 0u, 0u, 0u};
             if (row < rows) {
-                const uint16_t* src = row < a.Hq ? qin + row * D : kin + (row - a.Hq) * D;
+                const uint16_t* src = row < a.Hq        ? qin + row * D
+                                      : row < a.Hq + nk ? kin + (row - a.Hq) * D
+                                                        : vin + (row - a.Hq - nk) * D;
                 raw[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + f0));
             }
         }
@@ -134,6 +140,10 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
             sincosf(a.angles[arow * HALF + r], &s, &c);
             cs[r] = c;
             sn[r] = s;
+            if (a.cs_out && b == 0) {  // the table the attention's fused query RoPE reads
+                a.cs_out[(int64_t)p * D + r] = c;
+                a.cs_out[(int64_t)p * D + HALF + r] = s;
+            }
         }
     }
     __syncthreads();
@@ -171,7 +181,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
                 if (row < a.Hq) sq += ss;
-                else sk += ss;
+                else if (row < a.Hq + nk) sk += ss;
             }
         }
         __shared__ float red[2][kThreads / 64];
@@ -199,13 +209,15 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
     float gq[8], gk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) gq[e] = gk[e] = 1.f;
-    if constexpr (NORM == 1) {  // uniform: two 16-byte loads per weight vector
-        const f32x4* pq = reinterpret_cast<const f32x4*>(a.gamma_q + f0);
-        const f32x4 q0 = pq[0], q1 = pq[1];
+    if constexpr (NORM == 1) {  // uniform: two 16-byte loads per weight vector of the rows present
+        if (a.q_in) {
+            const f32x4* pq = reinterpret_cast<const f32x4*>(a.gamma_q + f0);
+            const f32x4 q0 = pq[0], q1 = pq[1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            gq[e] = q0[e];
-            gq[e + 4] = q1[e];
+            for (int e = 0; e < 4; ++e) {
+                gq[e] = q0[e];
+                gq[e + 4] = q1[e];
+            }
         }
         if (a.k_in) {
             const f32x4* pk = reinterpret_cast<const f32x4*>(a.gamma_k + f0);
@@ -225,6 +237,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
             if (base + nb * RPP >= rows_padded) break;  // uniform: past the last pass
             const bool valid = row < rows;
             const bool is_q = row < a.Hq;
+            const bool is_v = row >= a.Hq + nk;  // copied as is (uniform per row group)
             float z[8];
             unpack_bf16x8(raw[nb], z);
             if constexpr (NORM == 1) {
@@ -232,10 +245,10 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += z[e] * z[e];
                 ss = group_sum<LPR>(ss);
-                const float r = 1.f / sqrtf(ss / (float)D + a.eps);
+                const float r = is_v ? 1.f : 1.f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : gk[e]) * (z[e] * r);
-            } else if (NORM == 2 && valid) {
+                for (int e = 0; e < 8; ++e) z[e] = (is_q ? gq[e] : is_v ? 1.f : gk[e]) * (z[e] * r);
+            } else if (NORM == 2 && valid && !is_v) {
                 // weights of this row's features: gamma[h*d + f0 .. + 8]
                 const f32x4* pg = reinterpret_cast<const f32x4*>(
                     is_q ? a.gamma_q + row * D + f0 : a.gamma_k + (row - a.Hq) * D + f0);
@@ -247,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
                     z[e + 4] = g1[e] * (z[e + 4] * r);
                 }
             }
-            const int style = (is_q || a.rope_keys) ? a.rope_style : 0;  // uniform per row group
+            const int style = is_v ? 0 : (is_q || a.rope_keys) ? a.rope_style : 0;  // uniform per row group
             float o[8];
             if (style == 1) {
                 const bool first = li < LPR / 2;
@@ -268,7 +281,7 @@ __global__ void __launch_bounds__(kThreads, 3) qk_norm_rope_kernel(NormRopeArgs 
                 for (int e = 0; e < 8; ++e) o[e] = z[e];
             }
             if (valid) {
-                Out* dst = is_q ? qout + row * D : kout + (row - a.Hq) * D;
+                Out* dst = is_q ? qout + row * D : !is_v ? kout + (row - a.Hq) * D : vout + (row - a.Hq - nk) * D;
                 if constexpr (OUT8)
                     *reinterpret_cast<u32x2_t*>(dst + f0) = pack_e4m3x8(o);
                 else

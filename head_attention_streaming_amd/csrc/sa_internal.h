@@ -22,6 +22,8 @@ struct AttnArgs {
     int64_t ws_bytes;
     const float* gamma_q;  // optional RMSNorm weights [d] applied to each query row (null: none)
     float q_eps;
+    const float* q_cs;     // optional RoPE table [Lq, d] (cos then sin per row) after the norm
+    int q_rope;            // its pairing: 1 split, 2 interleaved
 };
 
 struct NormRopeArgs {
@@ -43,6 +45,10 @@ struct NormRopeArgs {
     int out_fp8;            // outputs are OCP FP8 E4M3 (1 byte) instead of bf16; strides in elements
     int ring_lc, ring_nsink, ring_nwin;  // ring_lc > 0: token p is physical row p of a rolling
     int64_t ring_chunk;                  // cache after chunk ring_chunk was written
+    const void* v_in;       // [B, L, Hkv, d] contiguous, or null: value rows copied (cast to the
+    void* v_out;            // output type) unnormalised and unrotated
+    int64_t v_out_bstride;
+    float* cs_out;          // [L, d] fp32, or null: cos then sin of token p's angles in row p
 };
 
 // Rolling sink + window cache after chunk c has been written (sizes in chunks of Lc tokens):

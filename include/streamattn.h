@@ -113,6 +113,31 @@ int qk_norm_rope_ex(const void* q_in, void* q_out, int64_t q_out_bstride,
                     int norm_scope, int rope_style, int out_dtype, void* stream);
 
 /*
+ * qk_norm_rope_v -- qk_norm_rope_ex that also copies the chunk's values and can write the
+ * cos/sin table of its angles: the per-chunk prologue of streaming self-attention in one launch
+ * (the Q/K prologue and the value half of the "K/V cache updates" of page
+ * "flashdreams.accelerated", section "Generic Multi Head Attention Interface").
+ *
+ * Arguments as qk_norm_rope_ex, and:
+ *   q_in, q_out  may both be NULL (no query rows; gamma_q must then be NULL and Hq is ignored),
+ *             for a caller that normalises the queries inside the attention (attn_forward_qnorm).
+ *   v_in      [B, L, Hkv, d] bf16 contiguous values, or NULL; v_out receives them unchanged
+ *             (rounded to E4M3 for out_dtype SA_DTYPE_FP8_E4M3) at v_out + b*v_out_bstride +
+ *             (p*Hkv + h)*d, e.g. a cache's value rows at the chunk's slot. NULL iff v_in is NULL.
+ *   rope_cs_out  fp32 [L, d], 16-byte aligned, device memory, or NULL: row p receives cos then
+ *             sin (fp32, as used for the keys) of the d/2 angles of position p -- the table
+ *             attn_forward_qnorm reads. Requires rope_style != SA_ROPE_NONE.
+ * At least one of q_in, k_in, v_in must be given. The keys are rotated unless rope_style has
+ * SA_ROPE_AFTER_CACHE; the values are never normalised or rotated.
+ */
+int qk_norm_rope_v(const void* q_in, void* q_out, int64_t q_out_bstride,
+                   const void* k_in, void* k_out, int64_t k_out_bstride,
+                   const void* v_in, void* v_out, int64_t v_out_bstride,
+                   const float* gamma_q, const float* gamma_k, const float* rope_angles, float* rope_cs_out,
+                   int B, int L, int Hq, int Hkv, int d, float eps,
+                   int norm_scope, int rope_style, int out_dtype, void* stream);
+
+/*
  * kv_cache_slot -- rolling sink + window cache: where chunk `chunk_idx` is written and how
  * many cached tokens the chunk then attends to. Pure host integer function (no device work).
  *
@@ -288,23 +313,27 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
- * attn_forward_qnorm -- attn_forward_ws with the query RMSNorm (head scope) fused into the
- * attention: each query row z is replaced by gamma_q * z / sqrt(mean(z^2) + eps), rounded once to
- * the query type, as it is loaded, and attended with. Page "flashdreams.accelerated", section
- * "Multi Head Attention Definition" (RMSNorm of Q before attention, per head; no RoPE here: the
- * cross-attention example normalises Q only) and equation of the attention itself there.
+ * attn_forward_qnorm -- attn_forward_ws with the query prologue fused into the attention: each
+ * query row z is replaced by gamma_q * z / sqrt(mean(z^2) + eps) (RMSNorm, head scope), then,
+ * when rope_style is SA_ROPE_SPLIT or SA_ROPE_INTERLEAVED, rotated by RoPE with the cos/sin
+ * table rope_cs, and rounded once to the query type as it is loaded and attended with. Page
+ * "flashdreams.accelerated", section "Multi Head Attention Definition" (RMSNorm of Q per head,
+ * then RoPE, before attention; the cross-attention example normalises Q without RoPE).
  *
- * q is read as given and not modified; the result equals qk_norm_rope(q, NORM_HEAD, ROPE_NONE)
- * followed by attn_forward_ws up to the summation order of the row's sum of squares (the
- * normalised query can differ by one ulp of the query type in rare rounding ties). gamma_q:
- * fp32 [d], 16-byte aligned, device memory. eps >= 0 and finite. dtype SA_DTYPE_BF16, SA_DTYPE_F16
- * or SA_DTYPE_BF16_F16V (FP8 queries: SA_ERR_UNSUPPORTED). Every other argument, the workspace
- * (may be NULL) and the errors as attn_forward_ws.
+ * q is read as given and not modified; the result equals qk_norm_rope (Q rows, head scope, the
+ * same angles) followed by attn_forward_ws, up to the summation order of the row's sum of
+ * squares (the normalised query can differ by one ulp of the query type in rare rounding ties).
+ *   gamma_q   fp32 [d], 16-byte aligned, device memory. eps >= 0 and finite.
+ *   rope_cs   fp32 [Lq, d], 16-byte aligned, device memory: row i holds cos then sin of query
+ *             row i's d/2 angles (the table qk_norm_rope_v writes), the same for every batch;
+ *             NULL with rope_style SA_ROPE_NONE (0).
+ * dtype SA_DTYPE_BF16, SA_DTYPE_F16 or SA_DTYPE_BF16_F16V (FP8 queries: SA_ERR_UNSUPPORTED).
+ * Every other argument, the workspace (may be NULL) and the errors as attn_forward_ws.
  */
 int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, const float* gamma_q, float eps,
-                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float scale, int window_left,
-                       int window_right, int64_t kv_bstride, int dtype, void* workspace, int64_t workspace_bytes,
-                       void* stream);
+                       const float* rope_cs, int rope_style, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                       float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                       void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Text describing the last non-zero status returned to this thread ("" if none). */
 const char* sa_last_error(void);

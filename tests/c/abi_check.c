@@ -47,8 +47,10 @@ int main(void) {
     CHECK(attn_forward((char*)p + 2, p, p, p, 1, 8, 8, 16, 16, 128, 0.1f, 0, NULL) == SA_ERR_ALIGN);
     CHECK(attn_forward_window(p, p, p, p, 1, 8, 8, 16, 16, 128, 0.1f, 3, -2, 16 * 8 * 128, SA_DTYPE_BF16, NULL) ==
           SA_ERR_RANGE);
-    CHECK(attn_forward_qnorm(p, p, p, p, NULL, 1e-6f, 1, 8, 8, 16, 16, 128, 0.1f, -1, -1, 16 * 8 * 128,
-                             SA_DTYPE_BF16, NULL, 0, NULL) == SA_ERR_NULL);
+    CHECK(attn_forward_qnorm(p, p, p, p, NULL, 1e-6f, NULL, SA_ROPE_NONE, 1, 8, 8, 16, 16, 128, 0.1f, -1, -1,
+                             16 * 8 * 128, SA_DTYPE_BF16, NULL, 0, NULL) == SA_ERR_NULL);
+    CHECK(qk_norm_rope_v(NULL, NULL, 0, NULL, NULL, 0, NULL, NULL, 0, NULL, NULL, NULL, NULL, 1, 16, 8, 8, 128, 1e-6f,
+                         SA_NORM_HEAD, SA_ROPE_NONE, SA_DTYPE_BF16, NULL) == SA_ERR_NULL);
     CHECK(attn_forward_workspace_bytes(96) == SA_ERR_UNSUPPORTED);
     /* empty problems are successful no-ops, whatever the pointers */
     CHECK(attn_forward(NULL, NULL, NULL, NULL, 1, 8, 8, 0, 16, 128, 0.1f, 0, NULL) == SA_OK);

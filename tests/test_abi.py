@@ -206,9 +206,9 @@ def test_attn_forward_qnorm_rejects_bad_arguments():
     L = lib()
     P, g = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
 
-    def call(gamma=g, eps=1e-6, Hq=8, Hkv=8, dtype=0, d=128):
-        return L.attn_forward_qnorm(P, P, P, P, gamma, eps, 1, Hq, Hkv, 16, 16, d, 0.1, -1, -1, 16 * Hkv * d, dtype,
-                                    None, 0, None)
+    def call(gamma=g, eps=1e-6, cs=None, style=0, Hq=8, Hkv=8, dtype=0, d=128):
+        return L.attn_forward_qnorm(P, P, P, P, gamma, eps, cs, style, 1, Hq, Hkv, 16, 16, d, 0.1, -1, -1,
+                                    16 * Hkv * d, dtype, None, 0, None)
 
     assert call(gamma=None) == -1
     assert call(gamma=ctypes.c_void_p(8192 + 4)) == -4
@@ -218,4 +218,33 @@ def test_attn_forward_qnorm_rejects_bad_arguments():
     assert call(dtype=9) == -3
     assert call(Hq=6, Hkv=4) == -2
     assert call(d=96) == -3
+    assert call(style=1) == -1          # RoPE without its cos/sin table
+    assert call(cs=g) == -1             # a table without a pairing
+    assert call(cs=g, style=3) == -3
+    assert call(cs=ctypes.c_void_p(8192 + 8), style=1) == -4
+    assert lib().sa_last_error().decode() != ""
+
+
+def test_qk_norm_rope_v_rejects_bad_arguments():
+    L = lib()
+    P, g, a = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    S = 64 * 8 * 128  # a cache of 64 rows
+
+    def call(q=(None, None), k=(P, P), v=(P, P), gq=None, gk=g, ang=a, cs=None, Hkv=8, d=128, style=1, out=0,
+             vbs=S, kbs=S, scope=1):
+        return L.qk_norm_rope_v(q[0], q[1], 16 * 8 * d, k[0], k[1], kbs, v[0], v[1], vbs, gq, gk, ang, cs, 1, 16, 8,
+                                Hkv, d, 1e-6, scope, style, out, None)
+
+    assert call(k=(None, None), v=(None, None)) == -1      # no rows at all
+    assert call(v=(P, None)) == -1                         # v_in without v_out
+    assert call(q=(P, None)) == -1
+    assert call(gq=g) == -2                                # query weights without queries
+    assert call(gk=None) == -1                             # key weights missing
+    assert call(cs=g, style=0, ang=None) == -2             # cos/sin table without RoPE
+    assert call(cs=ctypes.c_void_p(8192 + 4)) == -4
+    assert call(vbs=16 * 8 * 128 - 8) == -2                # value batch stride below one chunk
+    assert call(vbs=S + 8, out=2) == -2                    # FP8 strides must be 16-element multiples
+    assert call(Hkv=0) == -5
+    assert call(d=96) == -3
+    assert call(out=1) == -3
     assert lib().sa_last_error().decode() != ""

@@ -334,7 +334,9 @@ def test_kv_cache_append_casts_bit_exact(cache_dtype):
 
 
 def test_streaming_f16_v_cache_equals_bf16_cache():
-    """A cache that keeps V in f16 (bf16 K) gives bit-identical streaming outputs to a bf16 cache."""
+    """A cache that keeps V in f16 (bf16 K) gives bit-identical streaming outputs to a bf16 cache
+    (both on the separate route: the fused route applies to bf16 values only, and its in-kernel
+    query norm can round a query one ulp apart in rare ties)."""
     B, Lc, H, d, sink, window = 1, 120, 4, 128, 120, 360
     outs = {}
     for v_dtype in (None, torch.float16):
@@ -348,7 +350,7 @@ def test_streaming_f16_v_cache_equals_bf16_cache():
             ang = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d).to(DEV)
             q_buf = torch.empty_like(q)
             out = torch.empty_like(q)
-            binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5)
+            binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5, fuse=False)
             res.append(out.clone())
         torch.cuda.synchronize()
         outs[v_dtype] = res
@@ -458,3 +460,85 @@ def test_cross_attention_fused_query_norm_full_size():
 def zlib_seed(name: str) -> int:
     import zlib
     return zlib.crc32(name.encode()) % 10000
+
+
+@pytest.mark.parametrize("d,style,after,out8,with_q", [
+    (128, binding.SA_ROPE_SPLIT, False, False, False),
+    (64, binding.SA_ROPE_INTERLEAVED, False, False, True),
+    (128, binding.SA_ROPE_SPLIT, True, False, False),
+    (128, binding.SA_ROPE_SPLIT, False, True, False),
+    (64, binding.SA_ROPE_NONE, False, False, False),
+])
+def test_qk_norm_rope_v_matches_oracle(d, style, after, out8, with_q):
+    """The one-launch chunk prologue: keys normalised (rotated unless after-cache) within one ulp
+    of the oracle, values copied bit for bit (or rounded to E4M3 like the append), queries as in
+    qk_norm_rope, and the chunk's cos/sin table within a few fp32 ulps of cos/sin of the angles;
+    rows outside the slot untouched."""
+    B, L, Hq, Hkv, S, s0 = 2, 29, 6, 3, 96, 32
+    print(f"[case] d={d} style={style} after={after} out8={out8} with_q={with_q}", flush=True)
+    g = torch.Generator().manual_seed(500 + d + style + 2 * after + 4 * out8)
+    q = synthetic.normal((B, L, Hq, d), "bf16", g, 2.0)
+    k = synthetic.normal((B, L, Hkv, d), "bf16", g, 0.5)
+    v = synthetic.normal((B, L, Hkv, d), "bf16", g, 3.0)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    ang = synthetic.rope_angles(np.arange(900, 900 + L), d) if style else None
+    cdt = torch.float8_e4m3fn if out8 else torch.bfloat16
+    ck = torch.zeros((B, S, Hkv, d), dtype=cdt, device=DEV)
+    cv = torch.zeros_like(ck)
+    cs = torch.full((L, d), -7.0, device=DEV) if style else None
+    qo = torch.empty((B, L, Hq, d), dtype=cdt, device=DEV) if with_q else None
+    flag = binding.SA_ROPE_AFTER_CACHE if (after and style) else 0
+    binding.qk_norm_rope_v(k.to(DEV), ck[:, s0:], v.to(DEV), cv[:, s0:], gk.to(DEV), None if ang is None else ang.to(DEV),
+                           1e-6, binding.SA_NORM_HEAD, style | flag, rope_cs_out=cs, k_out_bstride=S * Hkv * d,
+                           v_out_bstride=S * Hkv * d, q_in=q.to(DEV) if with_q else None, q_out=qo,
+                           gamma_q=gq.to(DEV) if with_q else None)
+    torch.cuda.synchronize()
+    rnd = "e4m3" if out8 else "bf16"
+    kref = _oracle_prologue(k, gk, 1e-6, None if (after or not style) else ang, style)
+    assert_within_one_ulp(ck[:, s0:s0 + L].contiguous(), kref, "k")
+    vref = oracle.round_to(widen(v).reshape(v.shape), rnd)
+    got_v = widen(cv[:, s0:s0 + L].contiguous()).reshape(vref.shape)
+    assert np.array_equal(got_v, vref)
+    for t in (ck, cv):  # rows outside the slot stay zero
+        assert not t[:, :s0].float().abs().sum().item() and not t[:, s0 + L:].float().abs().sum().item()
+    if with_q:
+        assert_within_one_ulp(qo, _oracle_prologue(q, gq, 1e-6, ang, style), "q")
+    if style:
+        a64 = ang.double().numpy()
+        tab = cs.double().cpu().numpy()
+        assert np.abs(tab[:, :d // 2] - np.cos(a64)).max() < 4e-7
+        assert np.abs(tab[:, d // 2:] - np.sin(a64)).max() < 4e-7
+
+
+@pytest.mark.parametrize("style,after", [(binding.SA_ROPE_SPLIT, False), (binding.SA_ROPE_INTERLEAVED, False),
+                                         (binding.SA_ROPE_SPLIT, True)])
+def test_streaming_fused_route_equals_separate_route(style, after):
+    """stream_self_attention_step's fused route (one prologue launch for keys and values, the
+    query norm and RoPE inside the attention) against the separate route (prologue -> append ->
+    attention on the normalised queries), through fill and eviction: the caches are identical bit
+    for bit, the outputs within the attention bounds of each other."""
+    B, Lc, H, d, sink, window = 1, 96, 4, 128, 96, 192
+    print(f"[case] style={style} after={after}", flush=True)
+    caches = [binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after) for _ in range(2)]
+    for cch in caches:
+        cch.k.zero_()
+        cch.v.zero_()
+    g = torch.Generator().manual_seed(77)
+    gq, gk = synthetic.norm_weight(d, g).to(DEV), synthetic.norm_weight(d, g).to(DEV)
+    for c in range(6):
+        gc = torch.Generator().manual_seed(7000 + c)
+        q, k, v = (synthetic.normal((B, Lc, H, d), "bf16", gc).to(DEV) for _ in range(3))
+        n = min((c + 1) * Lc, sink + window)
+        ang = synthetic.rope_angles(np.arange(n) if after else np.arange(c * Lc, (c + 1) * Lc), d).to(DEV)
+        outs = []
+        for fuse, cch in zip((True, False), caches):
+            q_buf = torch.empty_like(q)
+            out = torch.empty_like(q)
+            binding.stream_self_attention_step(cch, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5, style,
+                                               binding.SA_NORM_HEAD, fuse=fuse)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert torch.equal(caches[0].k.view(torch.int16), caches[1].k.view(torch.int16)), c
+        assert torch.equal(caches[0].v.view(torch.int16), caches[1].v.view(torch.int16)), c
+        diff = (outs[0].float() - outs[1].float()).abs()
+        assert diff.max().item() <= 8e-3 and diff.mean().item() <= 1e-4, (c, diff.max().item(), diff.mean().item())
