@@ -168,6 +168,12 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
     for _ in range(S // Lc):  # fill the cache before timing
         step()
 
+    # the step's route (stream_self_attention_step's default): Q, K and V through one prologue
+    # launch when the value cache has the key cache's type, else prologue + append; then attention
+    one_launch = vdt is None
+    info["route"] = ("qk_norm_rope_v (Q -> q_buf, K and V -> cache) + attention" if one_launch else
+                     "qk_norm_rope (Q -> q_buf, K -> cache) + kv_cache_append (V) + attention")
+
     def kern():
         keys = cache.k_rot if after else cache.k
         if ws is not None:
@@ -196,6 +202,13 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         rot["i"] += 1
         binding.kv_cache_append(None, v, None, cache.v, state["c"], 0, S)
 
+    def prologue_v():  # the one-launch prologue: queries, keys and values
+        q, k, v = sets[rot["i"] % nsets]
+        rot["i"] += 1
+        binding.qk_norm_rope_v(k, cache.k[:, slot:], v, cache.v[:, slot:], gk, q_ang, 1e-6, binding.SA_NORM_HEAD,
+                               binding.SA_ROPE_SPLIT | flag, k_out_bstride=S * w.Hkv * w.d,
+                               v_out_bstride=S * w.Hkv * w.d, q_in=q, q_out=q_buf, gamma_q=gq)
+
     elem = 2 * w.B * Lc * w.Hq * w.d  # bytes of one [B, Lc, H, d] bf16 tensor
     out_elem = elem // 2 if w.cache_dtype == "e4m3" else elem   # the same tensor in the cache type
     info["cache_dtype"] = w.cache_dtype
@@ -206,15 +219,19 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
                                2 * elem + 2 * out_elem + Lc * (w.d // 2) * 4 + 2 * w.Hq * w.d * 4),
         "kv_cache_append": (append, elem + out_elem),                            # v read + written
     }
+    if one_launch:  # q, k, v read (bf16) + written (cache type), angles, gammas
+        info["hbm_steps"]["qk_norm_rope_v"] = (prologue_v, 3 * elem + 3 * out_elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4)
     if after:
         def cache_rope():
             binding.kv_cache_rope(cache.k, cache.k_rot, angles[7], state["c"] - 1, Lc, 0, S, binding.SA_ROPE_SPLIT)
         kbytes = 2 * w.B * S * w.Hkv * w.d
         info["hbm_steps"]["kv_cache_rope"] = (cache_rope, 2 * kbytes + S * (w.d // 2) * 4)  # cache K read, k_rot written, angles
-        info["step"] = ("qk_norm_rope(Q rotated, K normalised->cache) + kv_cache_append(V) + "
-                        "kv_cache_rope(visible K -> k_rot) + attn_forward_kvstride, cache full")
+        info["step"] = (("qk_norm_rope_v(Q rotated, K normalised->cache, V->cache)" if one_launch else
+                         "qk_norm_rope(Q rotated, K normalised->cache) + kv_cache_append(V)") +
+                        " + kv_cache_rope(visible K -> k_rot) + attention, cache full")
     else:
-        info["step"] = "qk_norm_rope(Q,K->cache) + kv_cache_append(V) + attn_forward_kvstride, cache full"
+        info["step"] = (("qk_norm_rope_v(Q, K->cache, V->cache)" if one_launch else
+                         "qk_norm_rope(Q,K->cache) + kv_cache_append(V)") + " + attention, cache full")
     info["cache_tokens"] = S
     return w, step, kern, info, None
 

@@ -15,7 +15,7 @@ import torch
 from . import build as _build
 
 SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3, SA_DTYPE_BF16_F16V = 0, 1, 2, 3
-SA_ERR_UNSUPPORTED_CODE = -3
+SA_ERR_SHAPE_CODE, SA_ERR_UNSUPPORTED_CODE = -2, -3
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
 
@@ -230,6 +230,9 @@ def qk_norm_rope_v(k_in, k_out, v_in, v_out, gamma_k=None, angles=None, eps: flo
         v_out_bstride = L * Hkv * d
     if q_out_bstride is None:
         q_out_bstride = L * max(Hq, 1) * d
+    outs = [t for t in (q_out, k_out, v_out) if t is not None]
+    if any(t.dtype != outs[0].dtype for t in outs):
+        raise StreamAttnError("qk_norm_rope_v", SA_ERR_SHAPE_CODE, "q_out, k_out and v_out must share one dtype")
     out_dtype = _dtype_code(k_out if k_out is not None else v_out)
     _check("qk_norm_rope_v", lib().qk_norm_rope_v(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
                                                   k_out_bstride, _ptr(v_in), _ptr(v_out), v_out_bstride, _ptr(gamma_q),
@@ -331,19 +334,23 @@ class BlockKVCache:
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
                                rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None,
-                               fuse: bool = True):
+                               query_in_attention: bool = False):
     """One streaming self-attention chunk as library calls between before_update / after_update.
 
-    Fused route (default, for a bf16 cache with bf16 values and head-scope norm): qk_norm_rope_v
-    writes the normalised (rotated, unless after-cache RoPE) keys and the values into the
-    chunk's cache slot and the chunk's cos/sin table into cache.rope_cs in one launch; the
-    attention (attn_forward_qnorm) normalises and rotates the raw queries as it loads them, so
-    q_buf is not used. Other caches and fuse=False take the separate route:
-    qk_norm_rope (q_in -> q_buf, k_in -> cache keys at the chunk's slot) -> kv_cache_append
-    (v_in -> cache values) -> attention over the visible cache.
+    Default route: qk_norm_rope_v in one launch writes the normalised (and rotated, unless
+    after-cache RoPE) queries into q_buf, the normalised keys into the chunk's cache slot and the
+    values into the value cache; the attention then reads q_buf. It applies when the value cache
+    has the key cache's type (bf16 or FP8 E4M3); a cache with f16 values takes qk_norm_rope (q_in
+    -> q_buf, k_in -> cache keys) -> kv_cache_append (v_in -> cache values) instead, with the same
+    results bit for bit.
+    query_in_attention=True (bf16 cache with bf16 values, head-scope norm, bf16 q_in): the
+    prologue writes keys, values and the chunk's cos/sin table (cache.rope_cs), and the attention
+    (attn_forward_qnorm) normalises and rotates the raw queries as it loads them; q_buf is not
+    used. This saves the query pass but reads the cos/sin table once per query block and head,
+    which on the streaming shapes costs more than the pass it saves.
     A cache of float8_e4m3fn (BlockKVCache(dtype=torch.float8_e4m3fn), before-cache RoPE only) with
-    an E4M3 q_buf is the FP8 path: the prologue rounds Q and K to E4M3, the append rounds V, and
-    attention runs on the FP8 MFMA with a bf16 out.
+    an E4M3 q_buf is the FP8 path: the prologue rounds Q, K and V to E4M3 and attention runs on
+    the FP8 MFMA with a bf16 out.
     Before-cache RoPE (cache.k_rot is None): angles [Lc, d/2] for the chunk's positions.
     After-cache RoPE (cache built with after_cache_rope=True): angles [visible_len, d/2] by
     logical row; the queries are rotated with the chunk's rows (the last Lc) and the keys are
@@ -360,26 +367,31 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
                               "after-cache RoPE is built for a bf16 cache only")
     q_angles = angles[visible - cache.chunk_len:visible] if after else angles
     flag = SA_ROPE_AFTER_CACHE if after else 0
-    fused = (fuse and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
-             cache.v.dtype == torch.bfloat16 and q_in.dtype == torch.bfloat16)
-    if fused:
-        rope = rope_style != SA_ROPE_NONE
+    rope = rope_style != SA_ROPE_NONE
+    style = (rope_style | flag) if rope else SA_ROPE_NONE
+    bstride = S * cache.Hkv * cache.d
+    in_attn = (query_in_attention and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
+               cache.v.dtype == torch.bfloat16 and q_in.dtype == torch.bfloat16)
+    if in_attn:
         qk_norm_rope_v(k_in, cache.k[:, slot:], v_in, cache.v[:, slot:], gamma_k, q_angles if rope else None, eps,
-                       norm_scope, (rope_style | flag) if rope else SA_ROPE_NONE,
-                       rope_cs_out=cache.rope_cs if rope else None, k_out_bstride=S * cache.Hkv * cache.d,
-                       v_out_bstride=S * cache.Hkv * cache.d)
+                       norm_scope, style, rope_cs_out=cache.rope_cs if rope else None, k_out_bstride=bstride,
+                       v_out_bstride=bstride)
+    elif cache.v.dtype == cache.k.dtype:
+        qk_norm_rope_v(k_in, cache.k[:, slot:], v_in, cache.v[:, slot:], gamma_k, q_angles if rope else None, eps,
+                       norm_scope, style, k_out_bstride=bstride, v_out_bstride=bstride, q_in=q_in, q_out=q_buf,
+                       gamma_q=gamma_q)
     else:
         qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
-                     norm_scope, rope_style | flag, k_out_bstride=S * cache.Hkv * cache.d)
+                     norm_scope, rope_style | flag, k_out_bstride=bstride)
         kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
     keys = cache.k
     if after:
         kv_cache_rope(cache.k, cache.k_rot, angles, chunk_idx, cache.chunk_len, cache.sink_size, cache.window_size,
                       rope_style)
         keys = cache.k_rot
-    if fused:
+    if in_attn:
         attn_forward_qnorm(q_in, keys, cache.v, out, scale, gamma_q, eps, workspace=workspace, Lk=visible,
-                           rope_cs=cache.rope_cs if rope_style != SA_ROPE_NONE else None, rope_style=rope_style)
+                           rope_cs=cache.rope_cs if rope else None, rope_style=rope_style)
     elif workspace is not None:
         attn_forward_ws(q_buf, keys, cache.v, out, scale, workspace, Lk=visible)
     else:

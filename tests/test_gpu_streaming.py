@@ -335,8 +335,8 @@ def test_kv_cache_append_casts_bit_exact(cache_dtype):
 
 def test_streaming_f16_v_cache_equals_bf16_cache():
     """A cache that keeps V in f16 (bf16 K) gives bit-identical streaming outputs to a bf16 cache
-    (both on the separate route: the fused route applies to bf16 values only, and its in-kernel
-    query norm can round a query one ulp apart in rare ties)."""
+    (the f16 cache takes the two-launch prologue, the bf16 one the one-launch prologue; both
+    attend on the same normalised queries)."""
     B, Lc, H, d, sink, window = 1, 120, 4, 128, 120, 360
     outs = {}
     for v_dtype in (None, torch.float16):
@@ -350,7 +350,7 @@ def test_streaming_f16_v_cache_equals_bf16_cache():
             ang = synthetic.rope_angles(np.arange(c * Lc, (c + 1) * Lc), d).to(DEV)
             q_buf = torch.empty_like(q)
             out = torch.empty_like(q)
-            binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5, fuse=False)
+            binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5)
             res.append(out.clone())
         torch.cuda.synchronize()
         outs[v_dtype] = res
@@ -510,16 +510,36 @@ def test_qk_norm_rope_v_matches_oracle(d, style, after, out8, with_q):
         assert np.abs(tab[:, d // 2:] - np.sin(a64)).max() < 4e-7
 
 
+def _two_launch_step(cache, c, q, k, v, q_buf, out, gq, gk, ang, scale, style):
+    """The chunk step composed from the separate calls: qk_norm_rope (Q -> q_buf, K -> cache
+    slot), kv_cache_append (V), kv_cache_rope (after-cache RoPE), attention on q_buf."""
+    slot, visible = cache.before_update(c)
+    after = cache.k_rot is not None
+    q_ang = ang[visible - cache.chunk_len:visible] if after else ang
+    flag = binding.SA_ROPE_AFTER_CACHE if after else 0
+    binding.qk_norm_rope(q, q_buf, k, cache.k[:, slot:], gq, gk, q_ang, 1e-6, binding.SA_NORM_HEAD, style | flag,
+                         k_out_bstride=cache.capacity * cache.Hkv * cache.d)
+    binding.kv_cache_append(None, v, None, cache.v, c, cache.sink_size, cache.window_size)
+    keys = cache.k
+    if after:
+        binding.kv_cache_rope(cache.k, cache.k_rot, ang, c, cache.chunk_len, cache.sink_size, cache.window_size,
+                              style)
+        keys = cache.k_rot
+    binding.attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
+    cache.after_update(c)
+
+
 @pytest.mark.parametrize("style,after", [(binding.SA_ROPE_SPLIT, False), (binding.SA_ROPE_INTERLEAVED, False),
                                          (binding.SA_ROPE_SPLIT, True)])
-def test_streaming_fused_route_equals_separate_route(style, after):
-    """stream_self_attention_step's fused route (one prologue launch for keys and values, the
-    query norm and RoPE inside the attention) against the separate route (prologue -> append ->
-    attention on the normalised queries), through fill and eviction: the caches are identical bit
-    for bit, the outputs within the attention bounds of each other."""
+def test_streaming_routes_agree(style, after):
+    """stream_self_attention_step's routes through fill and eviction: the default one-launch
+    prologue (qk_norm_rope_v: Q, K and V in one launch) equals the two-launch composition
+    (qk_norm_rope -> kv_cache_append) bit for bit in the caches and the outputs; the route with
+    the query norm and RoPE inside the attention (query_in_attention) leaves the same caches and
+    outputs within the attention bounds of the others."""
     B, Lc, H, d, sink, window = 1, 96, 4, 128, 96, 192
     print(f"[case] style={style} after={after}", flush=True)
-    caches = [binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after) for _ in range(2)]
+    caches = [binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after) for _ in range(3)]
     for cch in caches:
         cch.k.zero_()
         cch.v.zero_()
@@ -530,15 +550,18 @@ def test_streaming_fused_route_equals_separate_route(style, after):
         q, k, v = (synthetic.normal((B, Lc, H, d), "bf16", gc).to(DEV) for _ in range(3))
         n = min((c + 1) * Lc, sink + window)
         ang = synthetic.rope_angles(np.arange(n) if after else np.arange(c * Lc, (c + 1) * Lc), d).to(DEV)
-        outs = []
-        for fuse, cch in zip((True, False), caches):
-            q_buf = torch.empty_like(q)
-            out = torch.empty_like(q)
-            binding.stream_self_attention_step(cch, c, q, k, v, q_buf, out, gq, gk, ang, 1e-6, d ** -0.5, style,
-                                               binding.SA_NORM_HEAD, fuse=fuse)
-            outs.append(out)
+        outs = [torch.empty_like(q) for _ in range(3)]
+        bufs = [torch.empty_like(q) for _ in range(3)]
+        binding.stream_self_attention_step(caches[0], c, q, k, v, bufs[0], outs[0], gq, gk, ang, 1e-6, d ** -0.5,
+                                           style, binding.SA_NORM_HEAD)
+        _two_launch_step(caches[1], c, q, k, v, bufs[1], outs[1], gq, gk, ang, d ** -0.5, style)
+        binding.stream_self_attention_step(caches[2], c, q, k, v, bufs[2], outs[2], gq, gk, ang, 1e-6, d ** -0.5,
+                                           style, binding.SA_NORM_HEAD, query_in_attention=True)
         torch.cuda.synchronize()
-        assert torch.equal(caches[0].k.view(torch.int16), caches[1].k.view(torch.int16)), c
-        assert torch.equal(caches[0].v.view(torch.int16), caches[1].v.view(torch.int16)), c
-        diff = (outs[0].float() - outs[1].float()).abs()
+        for i in (1, 2):
+            assert torch.equal(caches[0].k.view(torch.int16), caches[i].k.view(torch.int16)), (c, i)
+            assert torch.equal(caches[0].v.view(torch.int16), caches[i].v.view(torch.int16)), (c, i)
+        assert torch.equal(bufs[0].view(torch.int16), bufs[1].view(torch.int16)), c
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), c
+        diff = (outs[0].float() - outs[2].float()).abs()
         assert diff.max().item() <= 8e-3 and diff.mean().item() <= 1e-4, (c, diff.max().item(), diff.mean().item())
