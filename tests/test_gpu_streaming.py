@@ -468,6 +468,7 @@ def zlib_seed(name: str) -> int:
     (128, binding.SA_ROPE_SPLIT, True, False, False),
     (128, binding.SA_ROPE_SPLIT, False, True, False),
     (64, binding.SA_ROPE_NONE, False, False, False),
+    (128, binding.SA_ROPE_SPLIT, False, True, True),   # the FP8 streaming step's prologue
 ])
 def test_qk_norm_rope_v_matches_oracle(d, style, after, out8, with_q):
     """The one-launch chunk prologue: keys normalised (rotated unless after-cache) within one ulp
