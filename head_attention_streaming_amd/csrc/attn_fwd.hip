@@ -468,19 +468,50 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         // raised issue priority until they are queued (measured +0.3 to +4 % across launch shapes).
         __builtin_amdgcn_s_setprio(1);
         if constexpr (QK) {
+            if constexpr (!FP8 && D == 64) {
+                // d = 64: the K fragment reads run four MFMAs ahead of their products, an issue
+                // order pinned for the scheduler (which otherwise waits on each read right
+                // before its MFMA). Measured +2-5 % at d = 64; at d = 128 it gains nothing and
+                // the extra registers cost the balanced launch 7-10 %.
+                constexpr int NQ = KB * DC, kLook = 4;
+                static_assert(NQ > kLook, "more products than reads in flight");
+                u32x4 kbuf[NQ];
+                auto kread = [&](int i) __attribute__((always_inline)) {
+                    kbuf[i] = kq_lane[((t & 1) * kBN * KST + (i / DC) * 32 * KST + 16 * (i % DC)) / 8];
+                };
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+                    for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
-                for (int cc = 0; cc < DC; ++cc) {
-                    if constexpr (FP8) {
-                        const int off = ((t & 1) * kBN * KST + kb * 32 * KST + 64 * cc) / 16;
-                        const u32x4 lo = kq_lane[off], hi = kq_lane[off + 1];
-                        sc[kb] = mfma_qk_fp8(__builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w})),
-                                             qf[cc], sc[kb]);
-                    } else {
-                        sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
+                for (int i = 0; i < kLook; ++i) kread(i);
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    if (i + kLook < NQ) kread(i + kLook);
+                    sc[i / DC] = mfma_qk<BF16>(kbuf[i], qf[i % DC], sc[i / DC]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, kLook, 0);  // kLook LDS reads
+#pragma unroll
+                for (int i = 0; i < NQ - kLook; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kLook, 0);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < DC; ++cc) {
+                        if constexpr (FP8) {
+                            const int off = ((t & 1) * kBN * KST + kb * 32 * KST + 64 * cc) / 16;
+                            const u32x4 lo = kq_lane[off], hi = kq_lane[off + 1];
+                            sc[kb] = mfma_qk_fp8(__builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w})),
+                                                 qf[cc], sc[kb]);
+                        } else {
+                            sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
+                        }
                     }
                 }
             }
