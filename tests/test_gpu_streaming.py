@@ -174,8 +174,10 @@ def test_kv_cache_append_bit_exact_fill_and_eviction(B, Lc, H, d, sink, window):
 
 
 def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, style=binding.SA_ROPE_SPLIT,
-                   after_cache=False, inner=False, fp8=False):
+                   after_cache=False, inner=False, fp8=False, workspace=False):
     """Run the streaming loop on the GPU and compare every chunk's output with the oracle.
+    workspace: pass an attention workspace, as the benchmark's steps do, so grids with a mostly
+    idle last round run balanced.
 
     Before-cache RoPE: angles at absolute stream positions c*Lc + i rotate the chunk's queries
     and keys, and the cache stores rotated keys. After-cache RoPE: the cache stores normalised,
@@ -193,6 +195,7 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
     scope = binding.SA_NORM_INNER if inner else binding.SA_NORM_HEAD
     kstar, vals = {}, {}
     results = []
+    ws = binding.attn_workspace(d) if workspace else None
     for c in range(n_chunks):
         gc = torch.Generator().manual_seed(seed0 + c)
         q = synthetic.normal((B, Lc, H, d), "bf16", gc)
@@ -208,7 +211,7 @@ def _streaming_run(B, Lc, H, d, sink, window, n_chunks, rows_per_chunk, seed0, s
         q_buf = torch.empty((B, Lc, H, d), dtype=cdt, device=DEV)
         out = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
         vis_len = binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, gqd, gkd,
-                                                     ang.to(DEV), eps, scale, style, scope)
+                                                     ang.to(DEV), eps, scale, style, scope, workspace=ws)
         torch.cuda.synchronize()
         # oracle: prologue in fp64, rounded once to the bf16 the cache stores; logical window
         qs = oracle.round_to(_oracle_prologue(q, gq, eps, ang_q, style, inner), rnd)
@@ -274,7 +277,7 @@ def test_streaming_after_cache_full_size_with_sink():
     w = synthetic.WORKLOADS["stream_self_1785x4"]
     print(f"[case] after-cache {w}", flush=True)
     _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=w.chunk, window=w.window - w.chunk, n_chunks=6,
-                   rows_per_chunk=512, seed0=w.seed + 50, after_cache=True)
+                   rows_per_chunk=512, seed0=w.seed + 50, after_cache=True, workspace=True)
 
 
 def test_streaming_fp8_cache_with_sink():
@@ -288,7 +291,7 @@ def test_streaming_fp8_cache_full_size():
     w = synthetic.WORKLOADS["stream_self_1785x4"]
     print(f"[case] fp8 {w}", flush=True)
     _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=0, window=w.window, n_chunks=6, rows_per_chunk=512,
-                   seed0=w.seed + 70, fp8=True)
+                   seed0=w.seed + 70, fp8=True, workspace=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -359,12 +362,14 @@ def test_streaming_f16_v_cache_equals_bf16_cache():
 
 
 def test_streaming_self_attention_full_size():
-    """Streaming self-attention at full size: chunks of 1785 tokens x 40 heads x 128, rolling cache
-    of 4 chunks (7140 keys), chunks 0-5 (fill, then eviction); sampled rows each chunk."""
+    """Streaming self-attention at full size, in the benchmark's configuration (one-launch
+    prologue, attention with a workspace, so the full cache's 280-block grid runs balanced):
+    chunks of 1785 tokens x 40 heads x 128, rolling cache of 4 chunks (7140 keys), chunks 0-5
+    (fill, then eviction); sampled rows each chunk."""
     w = synthetic.WORKLOADS["stream_self_1785x4"]
     print(f"[case] {w}", flush=True)
     _streaming_run(B=1, Lc=w.chunk, H=w.Hq, d=w.d, sink=0, window=w.window, n_chunks=6, rows_per_chunk=512,
-                   seed0=w.seed)
+                   seed0=w.seed, workspace=True)
 
 
 def test_cross_attention_full_size():
