@@ -691,28 +691,58 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         }
     }
 
-    // ---- epilogue: O / l, one rounding to the output dtype, 8-byte stores
+    // ---- epilogue: O / l, one rounding to the output dtype
     const float l = half_swap_sum(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qrow < p.Lq) {
+    auto packed = [&](int db, int rg) __attribute__((always_inline)) {  // features 32db + 8rg + 4g + [0, 4)
+        const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
+        const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
+        u32x2 w;
+        if constexpr (OUT_BF16) {
+            w.x = pack_bf16x2(x0, x1);
+            w.y = pack_bf16x2(x2, x3);
+        } else {
+            w.x = pack_f16x2(x0, x1);
+            w.y = pack_f16x2(x2, x3);
+        }
+        return w;
+    };
+    // Rows leave through LDS (free after the last step's barrier): each wave writes its 32 x D
+    // block to an area of its own, then stores whole rows, 16 bytes per lane. A lane's own
+    // features are 4 of every 8, so storing from registers would take 8-byte stores that touch
+    // 32 rows each; the whole-row stores need 8x fewer cache-line requests, which matters when
+    // every workgroup of a round stores at once (short key loops). Waves [0, NW/2) use the K
+    // tile array, the others the V tile array.
+    constexpr int OST = D + 8;         // LDS row stride of the output block (elements)
+    constexpr int kOArea = 32 * OST;   // elements per wave
+    constexpr bool kLdsOut = KS == 1 && !FP8 && (NW / 2) * kOArea * 2 <= (int)sizeof(Ks) &&
+                             (NW - NW / 2) * kOArea * 2 <= (int)sizeof(Vs);
+    if constexpr (kLdsOut) {
+        uint16_t* const area = wave < NW / 2 ? reinterpret_cast<uint16_t*>(&Ks[0][0]) + wave * kOArea
+                                             : &Vs[0][0] + (wave - NW / 2) * kOArea;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                *reinterpret_cast<u32x2*>(area + j * OST + 32 * db + 8 * rg + 4 * g) = packed(db, rg);
+        __syncthreads();
+        constexpr int kLpr = D / 8;        // lanes per row, 16 bytes each
+        constexpr int kRpi = 64 / kLpr;    // rows per store instruction
+        const int col = 8 * (lane % kLpr);
+        uint16_t* const ob = p.out + b * p.q_bstride + h * D + col;
+#pragma unroll
+        for (int i = 0; i < 32 / kRpi; ++i) {
+            const int rr = i * kRpi + lane / kLpr;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(area + rr * OST + col);
+            if (r0 + rr < p.Lq) *reinterpret_cast<u32x4*>(ob + (int64_t)(r0 + rr) * p.q_tstride) = val;
+        }
+        if constexpr (SK == 1) __syncthreads();  // the next unit stages its tiles into the same LDS
+    } else if (qrow < p.Lq) {
         uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int dcol = 32 * db + 8 * rg + 4 * g;
-                const float x0 = o[db][4 * rg + 0] * inv, x1 = o[db][4 * rg + 1] * inv;
-                const float x2 = o[db][4 * rg + 2] * inv, x3 = o[db][4 * rg + 3] * inv;
-                u32x2 w;
-                if constexpr (OUT_BF16) {
-                    w.x = pack_bf16x2(x0, x1);
-                    w.y = pack_bf16x2(x2, x3);
-                } else {
-                    w.x = pack_f16x2(x0, x1);
-                    w.y = pack_f16x2(x2, x3);
-                }
-                *reinterpret_cast<u32x2*>(op + dcol) = w;
-            }
+            for (int rg = 0; rg < 4; ++rg) *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * g) = packed(db, rg);
     }
     };  // unit
 
