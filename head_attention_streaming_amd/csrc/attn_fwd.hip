@@ -210,6 +210,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr int kKSlot = kBN * KST, kVSlot = kBN * VST;
     __shared__ __attribute__((aligned(16))) In Ks[KS][2 * kKSlot];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KS][2 * kVSlot];
+    // Output rows leave through LDS (see the epilogue): one area of 32 rows per row wave, waves
+    // [0, kRW/2) in the K tile array and the others in the V tile array, when they fit.
+    constexpr int OST = D + 8;         // LDS row stride of the output block (elements)
+    constexpr int kOArea = 32 * OST;   // elements per row wave
+    constexpr bool kLdsOut = !FP8 && (kRW / 2) * kOArea * 2 <= (int)sizeof(Ks) &&
+                             (kRW - kRW / 2) * kOArea * 2 <= (int)sizeof(Vs);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -670,7 +676,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + area[((db - d0) * 16 + r) * 64] * a1;
             }
-            if (d0 + DBR < DB) __syncthreads();  // the next round overwrites the area
+            // the next round overwrites the area, and after the last round the output rows
+            // pass through the same buffers
+            if (d0 + DBR < DB || kLdsOut) __syncthreads();
         }
         if (ks == 1) return;
     }
@@ -707,25 +715,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         }
         return w;
     };
-    // Rows leave through LDS (free after the last step's barrier): each wave writes its 32 x D
-    // block to an area of its own, then stores whole rows, 16 bytes per lane. A lane's own
-    // features are 4 of every 8, so storing from registers would take 8-byte stores that touch
-    // 32 rows each; the whole-row stores need 8x fewer cache-line requests, which matters when
-    // every workgroup of a round stores at once (short key loops). Waves [0, NW/2) use the K
-    // tile array, the others the V tile array.
-    constexpr int OST = D + 8;         // LDS row stride of the output block (elements)
-    constexpr int kOArea = 32 * OST;   // elements per wave
-    constexpr bool kLdsOut = KS == 1 && !FP8 && (NW / 2) * kOArea * 2 <= (int)sizeof(Ks) &&
-                             (NW - NW / 2) * kOArea * 2 <= (int)sizeof(Vs);
+    // Rows leave through LDS (free after the last step's or merge round's barrier): each row wave
+    // writes its 32 x D block to an area of its own, then stores whole rows, 16 bytes per lane. A
+    // lane's own features are 4 of every 8, so storing from registers would take 8-byte stores
+    // that touch 32 rows each; the whole-row stores need 8x fewer cache-line requests, which
+    // matters when every workgroup of a round stores at once (short key loops).
     if constexpr (kLdsOut) {
-        uint16_t* const area = wave < NW / 2 ? reinterpret_cast<uint16_t*>(&Ks[0][0]) + wave * kOArea
-                                             : &Vs[0][0] + (wave - NW / 2) * kOArea;
+        uint16_t* const area = rw < kRW / 2 ? reinterpret_cast<uint16_t*>(&Ks[0][0]) + rw * kOArea
+                                            : &Vs[0][0] + (rw - kRW / 2) * kOArea;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg)
                 *reinterpret_cast<u32x2*>(area + j * OST + 32 * db + 8 * rg + 4 * g) = packed(db, rg);
-        __syncthreads();
+        // only this wave reads its area: its writes complete before its reads are issued
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         constexpr int kLpr = D / 8;        // lanes per row, 16 bytes each
         constexpr int kRpi = 64 / kLpr;    // rows per store instruction
         const int col = 8 * (lane % kLpr);
