@@ -155,9 +155,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 //     otherwise leave CUs idle;
 //   8 waves as two key groups of 4 (128 rows, each group half of the keys): for grids with at
 //     most one 128-row workgroup per CU.
-// Keys per tile for a group of RW row waves: 32 for d = 128 with 4 row waves, 64 otherwise.
+// Keys per tile: 64 for every shape (at d = 128 a 4-wave workgroup's double-buffered K/V tiles
+// take 75.8 KB of LDS, two workgroups per CU still fit; against 32-key tiles: cross-attention
+// 1785 x 512 keys 3 % faster, d = 128 windows and causal within 2 %).
 template <int D, int RW>
-constexpr int tile_keys() { return (RW == 4 && D == 128) ? 32 : 64; }
+constexpr int tile_keys() { return 64; }
 
 // 32-bit words a lane hands over for one partial unit: its O^T accumulators divided by the
 // unit's row sum, as f16 pairs (a weighted mean of V rows, so within V's f16 range), then the
