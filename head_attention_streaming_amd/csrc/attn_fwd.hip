@@ -155,11 +155,10 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 //     otherwise leave CUs idle;
 //   8 waves as two key groups of 4 (128 rows, each group half of the keys): for grids with at
 //     most one 128-row workgroup per CU.
-// Keys per tile: 64 for every shape (at d = 128 a 4-wave workgroup's double-buffered K/V tiles
-// take 75.8 KB of LDS, two workgroups per CU still fit; against 32-key tiles: cross-attention
-// 1785 x 512 keys 3 % faster, d = 128 windows and causal within 2 %).
-template <int D, int RW>
-constexpr int tile_keys() { return 64; }
+// Keys per tile, every shape (at d = 128 a 4-wave workgroup's double-buffered K/V tiles take
+// 75.8 KB of LDS, so two workgroups per CU still fit; against 32-key tiles for that shape:
+// cross-attention 1785 x 512 keys 1.5-3 % faster, d = 128 windows and causal within 2 %).
+constexpr int kTileKeys = 64;
 
 // 32-bit words a lane hands over for one partial unit: its O^T accumulators divided by the
 // unit's row sum, as f16 pairs (a weighted mean of V rows, so within V's f16 range), then the
@@ -189,7 +188,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr int kRW = NW / KS;          // row waves per key group
     constexpr int kGThreads = kRW * 64;   // threads of one key group (they stage its tiles)
     constexpr int kBM = kRW * 32;         // query rows per workgroup
-    constexpr int kBN = tile_keys<D, kRW>();
+    constexpr int kBN = kTileKeys;
     constexpr int KB = kBN / 32;  // 32-key score blocks per tile
     constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
     // LDS row stride of a K tile (input elements): 16 bytes of padding keep the b128 reads of
@@ -952,7 +951,7 @@ hipError_t launch_balanced(const AttnArgs& a, int wgs, hipStream_t stream) {
     constexpr int NW = kBalancedWaves;
     KParams p = make_params<D, DT, NW, 1>(a);
     const int units = p.nblocks;
-    p.sk_tiles = (a.Lk + tile_keys<D, NW>() - 1) / tile_keys<D, NW>();
+    p.sk_tiles = (a.Lk + kTileKeys - 1) / kTileKeys;
     p.sk_wgs = wgs;
     p.sk_full = units / wgs;
     const int surplus = units - p.sk_full * wgs;  // > 0: balanced_pays requires a partial last round
@@ -985,7 +984,7 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     if (((int64_t)a.Lk + 64) * a.Hkv * D * elem > 0xffffffffLL) return launch<D, DT, 8, 1, true>(a, stream);
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
-    const int tiles8 = (a.Lk + tile_keys<D, 8>() - 1) / tile_keys<D, 8>();
+    const int tiles8 = (a.Lk + kTileKeys - 1) / kTileKeys;
     if (a.ws && a.ws_bytes >= balanced_workspace_bytes(a.d, (int)cus) && balanced_pays(a, wg256, cus, tiles8))
         return launch_balanced<D, DT>(a, (int)cus, stream);
     // Banded rows -- a window of at most 2048 + 1 keys, or causal rows of at most 4096 keys --
