@@ -278,6 +278,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         key_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, pos + p.win_right) : p.Lk - 1;
     }
     const unsigned key_span = (unsigned)(key_hi - key_lo);
+    // keys some row of this wave can see, [wave_lo, wave_hi] (rows past Lq only widen it): an
+    // edge tile outside it is skipped by this wave (its MFMAs, softmax and P*V), while the wave
+    // still stages tiles and meets every barrier
+    const int wave_lo = p.win_left >= 0 ? (int)max64(0, (int64_t)r0 + shift - p.win_left) : 0;
+    const int wave_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, (int64_t)r0 + 31 + shift + p.win_right) : p.Lk - 1;
+    auto dead_tile = [&](int tt) __attribute__((always_inline)) { return tt * kBN > wave_hi || tt * kBN + kBN - 1 < wave_lo; };
 
     // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row (16-bit
     // inputs), or [64c + 32g, 64c + 32g + 32) (FP8, two 16-byte loads per MFMA).
@@ -473,8 +479,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value, MASK = decltype(do_mask)::value;
         // This wave's S = K Q^T products issue ahead of the other wave's softmax work on the SIMD:
         // raised issue priority until they are queued (measured +0.3 to +4 % across launch shapes).
+        const bool qk_dead = QK && MASK && dead_tile(t);   // uniform over the wave
+        const bool pv_dead = PV && MASK && dead_tile(t - 1);
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (QK) {
+        if (QK && !qk_dead) {
             if constexpr (!FP8 && D == 64) {
                 // d = 64: the K fragment reads run four MFMAs ahead of their products, an issue
                 // order pinned for the scheduler (which otherwise waits on each read right
@@ -524,7 +532,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if constexpr (PV) {
+        if (PV && !pv_dead) {
             // P(t-1) as f16 operands; the row sum adds the f16 values the product uses
             const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
             float acc0 = 0.f, acc1 = 0.f;
@@ -552,7 +560,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             load_k(min(t + 2, nkt - 1));
             load_v(min(t + 1, nkt - 1));
         }
-        if constexpr (PV) {
+        if (PV && !pv_dead) {
             const int slot = (t - 1) & 1;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
@@ -566,7 +574,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                                                                     __builtin_bit_cast(f16x8, pf[kc]), o[db], 0, 0, 0);
                 }
         }
-        if constexpr (QK) {
+        if (QK && !qk_dead) {
             if constexpr (MASK) {
                 // one unsigned compare and a select per score: key - key_lo in [0, key_span]
                 const int rel0 = t * kBN + 4 * g - key_lo;
@@ -629,14 +637,25 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             if (mask0) step(T_{}, F_{}, T_{}, ta, s0, s1);
             else step(T_{}, F_{}, F_{}, ta, s0, s1);
         }
-        // steps ta+1 .. tend-1 in three segments: left-edge masked, unmasked, right-edge masked
-        const int e1 = min(max(tl, ta + 1), tend);
+        // steps ta+1 .. tend-1 in three segments: left-edge masked, unmasked, right-edge masked.
+        // A masked step also decides whether this wave skips the previous tile's softmax and
+        // P*V, so when the tile before the unmasked run is masked, the run starts one step later
+        // (that step's mask passes every score).
+        auto masked = [&](int tt) __attribute__((always_inline)) { return tt < tl || tt >= tr; };
+        int e1 = min(max(tl, ta + 1), tend);
         const int e2 = max(e1, min(tr, tend));
+        if (e1 < e2 && masked(e1 - 1)) ++e1;
         middle(T_{}, ta + 1, e1);
         middle(F_{}, e1, e2);
         middle(T_{}, e2, tend);
-        if (tend & 1) step(F_{}, T_{}, F_{}, tend, s1, s0);  // S(tend-1) in s0 when tend-1 is even
-        else step(F_{}, T_{}, F_{}, tend, s0, s1);
+        const bool mlast = masked(tend - 1);
+        if (tend & 1) {  // S(tend-1) in s0 when tend-1 is even
+            if (mlast) step(F_{}, T_{}, T_{}, tend, s1, s0);
+            else step(F_{}, T_{}, F_{}, tend, s1, s0);
+        } else {
+            if (mlast) step(F_{}, T_{}, T_{}, tend, s0, s1);
+            else step(F_{}, T_{}, F_{}, tend, s0, s1);
+        }
     }
 
     if constexpr (KS == 2) {
