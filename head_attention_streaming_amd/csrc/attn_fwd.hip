@@ -284,6 +284,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     const int wave_lo = p.win_left >= 0 ? (int)max64(0, (int64_t)r0 + shift - p.win_left) : 0;
     const int wave_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, (int64_t)r0 + 31 + shift + p.win_right) : p.Lk - 1;
     auto dead_tile = [&](int tt) __attribute__((always_inline)) { return tt * kBN > wave_hi || tt * kBN + kBN - 1 < wave_lo; };
+    // Balanced launches have no windows or causal masks (only key tails), so no tile is dead
+    // there; their kernel, at its register limit, keeps the plain sequence of steps.
+    constexpr bool kSkipDead = SK == 0;
 
     // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row (16-bit
     // inputs), or [64c + 32g, 64c + 32g + 32) (FP8, two 16-byte loads per MFMA).
@@ -479,8 +482,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value, MASK = decltype(do_mask)::value;
         // This wave's S = K Q^T products issue ahead of the other wave's softmax work on the SIMD:
         // raised issue priority until they are queued (measured +0.3 to +4 % across launch shapes).
-        const bool qk_dead = QK && MASK && dead_tile(t);   // uniform over the wave
-        const bool pv_dead = PV && MASK && dead_tile(t - 1);
+        const bool qk_dead = kSkipDead && QK && MASK && dead_tile(t);   // uniform over the wave
+        const bool pv_dead = kSkipDead && PV && MASK && dead_tile(t - 1);
         __builtin_amdgcn_s_setprio(1);
         if (QK && !qk_dead) {
             if constexpr (!FP8 && D == 64) {
@@ -644,11 +647,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         auto masked = [&](int tt) __attribute__((always_inline)) { return tt < tl || tt >= tr; };
         int e1 = min(max(tl, ta + 1), tend);
         const int e2 = max(e1, min(tr, tend));
-        if (e1 < e2 && masked(e1 - 1)) ++e1;
+        if (kSkipDead && e1 < e2 && masked(e1 - 1)) ++e1;
         middle(T_{}, ta + 1, e1);
         middle(F_{}, e1, e2);
         middle(T_{}, e2, tend);
-        const bool mlast = masked(tend - 1);
+        const bool mlast = kSkipDead && masked(tend - 1);
         if (tend & 1) {  // S(tend-1) in s0 when tend-1 is even
             if (mlast) step(F_{}, T_{}, T_{}, tend, s1, s0);
             else step(F_{}, T_{}, F_{}, tend, s1, s0);
