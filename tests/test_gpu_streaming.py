@@ -571,3 +571,33 @@ def test_streaming_routes_agree(style, after):
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), c
         diff = (outs[0].float() - outs[2].float()).abs()
         assert diff.max().item() <= 8e-3 and diff.mean().item() <= 1e-4, (c, diff.max().item(), diff.mean().item())
+
+
+@pytest.mark.parametrize("v_dtype", [None, torch.float16], ids=["one_launch", "two_launch"])
+def test_streaming_without_norm_or_rope(v_dtype):
+    """The streaming step with neither RMSNorm nor RoPE (no weights, no angles), on both prologue
+    routes: the cache holds the raw keys and values, and each chunk's output is plain attention
+    of the raw queries over the visible chunks (oracle rolling-cache model), through eviction."""
+    B, Lc, H, d, sink, window = 2, 48, 2, 64, 48, 96
+    print(f"[case] no norm, no rope, v_dtype={v_dtype}", flush=True)
+    cache = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, v_dtype=v_dtype)
+    model = RollingCacheModel(Lc, sink, window)
+    keys, vals = {}, {}
+    for c in range(6):
+        gc = torch.Generator().manual_seed(6100 + c)
+        q, k, v = (synthetic.normal((B, Lc, H, d), "bf16", gc) for _ in range(3))
+        q_buf = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty_like(q_buf)
+        vis_len = binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, None, None,
+                                                     None, 1e-6, d ** -0.5, binding.SA_ROPE_NONE, binding.SA_NORM_NONE)
+        torch.cuda.synchronize()
+        model.write(c)
+        keys[c], vals[c] = widen(k).reshape(k.shape), widen(v).reshape(v.shape)
+        vis = model.visible_chunks()
+        assert vis_len == model.visible_len()
+        ref = oracle.attention(widen(q).reshape(q.shape), np.concatenate([keys[x] for x in vis], axis=1),
+                               np.concatenate([vals[x] for x in vis], axis=1), d ** -0.5)
+        assert_attention_close(out, ref, f"chunk {c}")
+        s0 = model.slot_of(c)
+        assert np.array_equal(widen(cache.k[:, s0:s0 + Lc]).reshape(k.shape), keys[c])
+        assert np.array_equal(widen(q_buf).reshape(q.shape), widen(q).reshape(q.shape))
