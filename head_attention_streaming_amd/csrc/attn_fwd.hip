@@ -286,7 +286,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     auto dead_tile = [&](int tt) __attribute__((always_inline)) { return tt * kBN > wave_hi || tt * kBN + kBN - 1 < wave_lo; };
     // Balanced launches have no windows or causal masks (only key tails), so no tile is dead
     // there; their kernel, at its register limit, keeps the plain sequence of steps.
-    constexpr bool kSkipDead = SK == 0;
+    constexpr bool kSkipDead = !SK;
 
     // Q^T operand: lane (g, j) holds features [16c + 8g, 16c + 8g + 8) of its row (16-bit
     // inputs), or [64c + 32g, 64c + 32g + 32) (FP8, two 16-byte loads per MFMA).
@@ -763,7 +763,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(area + rr * OST + col);
             if (r0 + rr < p.Lq) *reinterpret_cast<u32x4*>(ob + (int64_t)(r0 + rr) * p.q_tstride) = val;
         }
-        if constexpr (SK == 1) __syncthreads();  // the next unit stages its tiles into the same LDS
+        if constexpr (SK) __syncthreads();  // the next unit stages its tiles into the same LDS
     } else if (qrow < p.Lq) {
         uint16_t* op = p.out + b * p.q_bstride + (int64_t)qrow * p.q_tstride + h * D;
 #pragma unroll
