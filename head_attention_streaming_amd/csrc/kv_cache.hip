@@ -12,7 +12,9 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+// Two 16-byte vectors per thread: of 2, 4 and 8, the most workgroups in flight and the fastest
+// append of a 1785-token chunk (8.1 us against 8.3 and 15.4 for 36.6 MB).
+constexpr int kVecPerThread = 2;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
