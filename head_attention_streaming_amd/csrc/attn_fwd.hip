@@ -160,11 +160,13 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // cross-attention 1785 x 512 keys 1.5-3 % faster, d = 128 windows and causal within 2 %).
 constexpr int kTileKeys = 64;
 
-// 32-bit words a lane hands over for one partial unit: its O^T accumulators divided by the
-// unit's row sum, as f16 pairs (a weighted mean of V rows, so within V's f16 range), then the
-// running offset m and the row sum l of the piece's keys (fp32).
+// 16-byte chunks a lane hands over for one partial unit: its O^T accumulators divided by the
+// unit's row sum, as f16 pairs (a weighted mean of V rows, so within V's f16 range), two chunks
+// per 32-feature block, then one chunk holding the running offset m and the row sum l of the
+// piece's keys (fp32). Chunk c of the wave's 64 lanes is 1 KB contiguous ([chunk][lane]), so
+// every hand-over store and merge load is 16 bytes per lane and coalesced.
 template <int D>
-constexpr int partial_words() { return 8 * (D / 32) + 2; }
+constexpr int partial_chunks() { return 2 * (D / 32) + 1; }
 
 // Integer min / max of 64-bit values (in device code the generic min / max of int64_t go through
 // double precision).
@@ -708,16 +710,19 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 
     if constexpr (SK) {
         if (part_slot >= 0) {  // split unit: hand over O / l, m, l (merged by attn_merge_kernel)
-            constexpr int NV = partial_words<D>();
-            uint32_t* dst = reinterpret_cast<uint32_t*>(p.ws) + ((int64_t)part_slot * NW + wave) * NV * 64 + lane;
+            constexpr int NC = partial_chunks<D>();
+            u32x4* dst = reinterpret_cast<u32x4*>(p.ws) + ((int64_t)part_slot * NW + wave) * NC * 64 + lane;
             const float lt = half_swap_sum(l_run);
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            auto pk = [&](int db, int i) __attribute__((always_inline)) {
+                return pack_f16x2(o[db][2 * i] * inv, o[db][2 * i + 1] * inv);
+            };
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dst[(8 * db + i) * 64] = pack_f16x2(o[db][2 * i] * inv, o[db][2 * i + 1] * inv);
-            dst[8 * DB * 64] = __float_as_uint(m_run);
-            dst[(8 * DB + 1) * 64] = __float_as_uint(lt);
+                for (int hh = 0; hh < 2; ++hh)
+                    dst[(2 * db + hh) * 64] = u32x4{pk(db, 4 * hh), pk(db, 4 * hh + 1), pk(db, 4 * hh + 2), pk(db, 4 * hh + 3)};
+            dst[2 * DB * 64] = u32x4{__float_as_uint(m_run), __float_as_uint(lt), 0u, 0u};
             return;
         }
     }
@@ -805,7 +810,7 @@ template <int D, int DT, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     constexpr bool OUT_BF16 = DT != kDtF16;
     constexpr int DB = D / 32;
-    constexpr int NV = partial_words<D>();
+    constexpr int NC = partial_chunks<D>();
     constexpr int kBM = NW * 32;
     const int e = blockIdx.x / DB, db = blockIdx.x % DB;
     const int nT = p.sk_tiles, P = p.sk_wgs;
@@ -820,9 +825,9 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     const int rem0 = (int)(p.sk_work * w0 % P);
     const int64_t step_q = p.sk_work / P;
     const int step_r = (int)(p.sk_work % P);
-    const uint32_t* base = reinterpret_cast<const uint32_t*>(p.ws) + (int64_t)wave * NV * 64 + lane;
-    constexpr int64_t kSlot = (int64_t)NW * NV * 64;
-    const uint32_t* first = base + (beg0 >= lo ? 2 * w0 : 2 * w0 + 1) * kSlot;
+    const u32x4* base = reinterpret_cast<const u32x4*>(p.ws) + (int64_t)wave * NC * 64 + lane;
+    constexpr int64_t kSlot = (int64_t)NW * NC * 64;
+    const u32x4* first = base + (beg0 >= lo ? 2 * w0 : 2 * w0 + 1) * kSlot;
     // the pieces of workgroups w0, w0 + 1, ... that start before hi, stepping
     // w_begin(w + 1) = w_begin(w) + step_q (+1 when the remainder of sk_work * w wraps)
     auto next = [&](int64_t& beg, int& rem) __attribute__((always_inline)) {
@@ -859,11 +864,11 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
     float o[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    each_piece([&](const uint32_t* src, bool ne) {
-        const float mv = __uint_as_float(src[8 * DB * 64]), lv = __uint_as_float(src[(8 * DB + 1) * 64]);
-        uint32_t ow[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ow[i] = src[(8 * db + i) * 64];
+    each_piece([&](const u32x4* src, bool ne) {
+        const u32x4 ml = src[2 * DB * 64];
+        const float mv = __uint_as_float(ml.x), lv = __uint_as_float(ml.y);
+        const u32x4 c0 = src[(2 * db) * 64], c1 = src[(2 * db + 1) * 64];
+        const uint32_t ow[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         const float mi = ne ? mv : -1e30f;
         const float mn = fmaxf(M, mi);
         const float a = __builtin_amdgcn_exp2f(M - mn);
@@ -904,7 +909,7 @@ constexpr int kBalancedWaves = 8;
 
 // Workspace of a balanced launch: two partial slots per workgroup, one per wave and lane.
 int64_t balanced_workspace_bytes(int d, int wgs) {
-    return (int64_t)2 * wgs * kBalancedWaves * 64 * (8 * (d / 32) + 2) * (int64_t)sizeof(uint32_t);
+    return (int64_t)2 * wgs * kBalancedWaves * 64 * (2 * (d / 32) + 1) * (int64_t)sizeof(u32x4);
 }
 
 // A balanced launch pays when the grid's rounds would keep the slots under 90 % busy, for

@@ -286,7 +286,7 @@ int attn_forward_window(const void* q, const void* k, const void* v, void* out,
 /*
  * attn_forward_workspace_bytes -- size of the workspace that lets attn_forward_ws balance any
  * launch of head dim d on the current device (two partial-result slots per persistent
- * workgroup, one workgroup per CU: 35.7 MB at d = 128 and 18.9 MB at d = 64 on 256 CUs).
+ * workgroup, one workgroup per CU: 37.7 MB at d = 128 and 21.0 MB at d = 64 on 256 CUs).
  * Returns the byte count, or SA_ERR_UNSUPPORTED for d not in {64, 128}. Host function.
  */
 int64_t attn_forward_workspace_bytes(int d);
