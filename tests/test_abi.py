@@ -248,3 +248,21 @@ def test_qk_norm_rope_v_rejects_bad_arguments():
     assert call(d=96) == -3
     assert call(out=1) == -3
     assert lib().sa_last_error().decode() != ""
+
+
+def test_binding_qk_norm_rope_v_requires_one_output_dtype():
+    """The one-launch prologue writes every output row in one type (the C-ABI takes a single
+    out_dtype), so the binding rejects query/key/value outputs of different dtypes before any
+    library call."""
+    import torch
+    from head_attention_streaming_amd import binding
+    k = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    q = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.qk_norm_rope_v(k, torch.empty_like(k), v, torch.empty_like(v, dtype=torch.float16))
+    assert e.value.status == binding.SA_ERR_SHAPE_CODE
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.qk_norm_rope_v(k, torch.empty_like(k), v, torch.empty_like(v), q_in=q,
+                               q_out=torch.empty_like(q, dtype=torch.float8_e4m3fn))
+    assert e.value.status == binding.SA_ERR_SHAPE_CODE
