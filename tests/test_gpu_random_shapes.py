@@ -82,3 +82,48 @@ def test_random_shape_matches_oracle(case):
         rows = sample_rows(B, Lq, Hq, nrows, seed=len(name) + Lq)
         ref = oracle.attention(Q, K, V, scale, window=window, rows=rows)
         assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name, ulp_floor=True)
+
+
+def _fp8_qnorm_cases():
+    rng = np.random.RandomState(31)
+    out = []
+    for i in range(12):
+        Lq = int(rng.choice([1, 64, 129, 257, 700, 1785]))
+        Lk = int(rng.choice([1, 63, 65, 512, 2100]))
+        Hkv = int(rng.choice([1, 2, 4])); Hq = Hkv * int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128])); B = int(rng.choice([1, 2]))
+        mode = ("fp8", "qnorm", "qnorm_ws")[i % 3]
+        causal = mode == "fp8" and Lq <= Lk and bool(rng.randint(2))
+        dtype = "e4m3" if mode == "fp8" else str(rng.choice(["bf16", "f16"]))
+        out.append((f"{mode}{i}", B, Lq, Lk, Hq, Hkv, d, dtype, causal))
+    return out
+
+
+FP8_QNORM_CASES = _fp8_qnorm_cases()
+
+
+@pytest.mark.parametrize("case", FP8_QNORM_CASES, ids=[c[0] for c in FP8_QNORM_CASES])
+def test_random_fp8_and_fused_query_norm_match_oracle(case):
+    """Seeded random shapes through the FP8 E4M3 path (attn_forward_fp8, full or causal) and the
+    fused query RMSNorm (attn_forward_qnorm, plain or with a workspace); sampled rows against the
+    oracle (for the norm: the oracle's RMSNorm rounded once to the query type, then attention)."""
+    name, B, Lq, Lk, Hq, Hkv, d, dtype, causal = case
+    print(f"[case] {case}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=3100 + len(FP8_QNORM_CASES) * Lq % 997)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    Q, K, V = (widen(x).reshape(x.shape) for x in (q, k, v))
+    rows = sample_rows(B, Lq, Hq, min(512, B * Lq * Hq), seed=Lq + Lk)
+    scale = d ** -0.5
+    if name.startswith("fp8"):
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+        binding.attn_forward_fp8(qd, kd, vd, out, scale, causal)
+        ref = oracle.attention(Q, K, V, scale, causal=causal, rows=rows)
+    else:
+        gq = synthetic.norm_weight(d, torch.Generator().manual_seed(Lq + 7))
+        out = torch.empty_like(qd)
+        ws = binding.attn_workspace(d) if name.startswith("qnorm_ws") else None
+        binding.attn_forward_qnorm(qd, kd, vd, out, scale, gq.to(DEV), 1e-6, workspace=ws)
+        qs = oracle.round_to(oracle.qk_norm_rope(Q, gq.double().numpy(), 1e-6, None, 0), dtype)
+        ref = oracle.attention(qs, K, V, scale, rows=rows)
+    torch.cuda.synchronize()
+    assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name, ulp_floor=True)
