@@ -93,6 +93,14 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _require_bf16(fn: str, *tensors) -> None:
+    """The prologue kernels read bf16 rows: any other input type would be misread (or, for a
+    one-byte type, read past its end)."""
+    for t in tensors:
+        if t is not None and t.dtype != torch.bfloat16:
+            raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE, f"inputs must be bfloat16, got {t.dtype}")
+
+
 def _attn_dtype(q, k, v) -> int:
     """Attention dtype code of (q, k, v): one common type, or bf16 q/k with an f16 v."""
     if q.dtype == torch.bfloat16 and k.dtype == torch.bfloat16 and v.dtype == torch.float16:
@@ -208,6 +216,12 @@ def qk_norm_rope(q_in, q_out, k_in=None, k_out=None, gamma_q=None, gamma_k=None,
         q_out_bstride = L * Hq * d
     if k_out_bstride is None:
         k_out_bstride = L * Hkv * d
+    # the C call takes one output type for both row classes and reads 16-bit inputs: a key output
+    # of another type would be written with the query output's element size
+    _require_bf16("qk_norm_rope", q_in, k_in)
+    if k_out is not None and k_out.dtype != q_out.dtype:
+        raise StreamAttnError("qk_norm_rope", SA_ERR_SHAPE_CODE,
+                              f"q_out ({q_out.dtype}) and k_out ({k_out.dtype}) must share one dtype")
     out_dtype = _dtype_code(q_out)
     _check("qk_norm_rope_ex", lib().qk_norm_rope_ex(_ptr(q_in), _ptr(q_out), q_out_bstride, _ptr(k_in), _ptr(k_out),
                                                     k_out_bstride, _ptr(gamma_q), _ptr(gamma_k), _ptr(angles), B, L,
@@ -230,6 +244,7 @@ def qk_norm_rope_v(k_in, k_out, v_in, v_out, gamma_k=None, angles=None, eps: flo
         v_out_bstride = L * Hkv * d
     if q_out_bstride is None:
         q_out_bstride = L * max(Hq, 1) * d
+    _require_bf16("qk_norm_rope_v", q_in, k_in, v_in)
     outs = [t for t in (q_out, k_out, v_out) if t is not None]
     if any(t.dtype != outs[0].dtype for t in outs):
         raise StreamAttnError("qk_norm_rope_v", SA_ERR_SHAPE_CODE, "q_out, k_out and v_out must share one dtype")
@@ -263,6 +278,7 @@ def kv_cache_rope(cache_k, k_rot, angles, chunk_idx: int, chunk_len: int, sink_s
     """After-cache RoPE: rotate the visible rows of cache_k [B, S, Hkv, d] into k_rot (same shape)
     with angles [visible_len, d/2] indexed by logical row."""
     B, S, Hkv, d = cache_k.shape
+    _require_bf16("kv_cache_rope", cache_k, k_rot)
     _check("kv_cache_rope", lib().kv_cache_rope(_ptr(cache_k), _ptr(k_rot), _ptr(angles), B, Hkv, d, int(chunk_len),
                                                 int(sink_size), int(window_size), int(chunk_idx), int(rope_style),
                                                 _stream(cache_k)))
@@ -271,17 +287,26 @@ def kv_cache_rope(cache_k, k_rot, angles, chunk_idx: int, chunk_len: int, sink_s
 def kv_cache_append(k_new, v_new, cache_k, cache_v, chunk_idx: int, sink_size: int, window_size: int):
     """Copy k_new / v_new [B, Lc, Hkv, d] (either may be None) into their cache slot range; a cache of
     another element type (float8_e4m3fn or f16 for bf16 input) receives the rounded values."""
-    ref = v_new if v_new is not None else k_new
-    dst = cache_v if v_new is not None else cache_k
-    B, Lc, Hkv, d = ref.shape
-    if ref.dtype == dst.dtype and ref.element_size() == 2:  # any 16-bit type: a byte copy
-        _check("kv_cache_append", lib().kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B,
-                                                        Lc, Hkv, d, sink_size, window_size, int(chunk_idx),
-                                                        _stream(ref)))
-        return
-    _check("kv_cache_append_ex", lib().kv_cache_append_ex(_ptr(k_new), _ptr(v_new), _ptr(cache_k), _ptr(cache_v), B,
-                                                          Lc, Hkv, d, sink_size, window_size, int(chunk_idx),
-                                                          _dtype_code(ref), _dtype_code(dst), _stream(ref)))
+    if k_new is None and v_new is None:
+        raise StreamAttnError("kv_cache_append", -1, "both k_new and v_new are None")
+    same = (k_new is None or v_new is None or
+            (k_new.dtype == v_new.dtype and cache_k.dtype == cache_v.dtype))
+    # one C call converts both tensors with one (source, cache) type pair, so keys and values of
+    # different type pairs (e.g. a bf16 key cache with an f16 value cache) take one call each
+    pairs = [(k_new, v_new, cache_k, cache_v)] if same else [(k_new, None, cache_k, None), (None, v_new, None, cache_v)]
+    for kn, vn, ck, cv in pairs:
+        ref = vn if vn is not None else kn
+        dst = cv if vn is not None else ck
+        if dst is None:
+            raise StreamAttnError("kv_cache_append", -1, "a cache tensor is None for a given source")
+        B, Lc, Hkv, d = ref.shape
+        if ref.dtype == dst.dtype and ref.element_size() == 2:  # any 16-bit type: a byte copy
+            _check("kv_cache_append", lib().kv_cache_append(_ptr(kn), _ptr(vn), _ptr(ck), _ptr(cv), B, Lc, Hkv, d,
+                                                            sink_size, window_size, int(chunk_idx), _stream(ref)))
+            continue
+        _check("kv_cache_append_ex", lib().kv_cache_append_ex(_ptr(kn), _ptr(vn), _ptr(ck), _ptr(cv), B, Lc, Hkv, d,
+                                                              sink_size, window_size, int(chunk_idx),
+                                                              _dtype_code(ref), _dtype_code(dst), _stream(ref)))
 
 
 class BlockKVCache:
@@ -331,6 +356,27 @@ class BlockKVCache:
         self._current = None
 
 
+def _check_step_dtypes(cache: BlockKVCache, q_in, k_in, v_in, q_buf, out, in_attn: bool) -> None:
+    """The type combinations a streaming step is built for, checked before its first launch:
+    bf16 inputs; a bf16 or E4M3 key cache whose value cache has the same type (or f16 values
+    with bf16 keys); queries buffered in the key cache's type; a bf16 output."""
+    fn = "stream_self_attention_step"
+    _require_bf16(fn, q_in, k_in, v_in)
+    kt, vt = cache.k.dtype, cache.v.dtype
+    if kt not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE, f"key cache dtype {kt} is not bf16 or float8_e4m3fn")
+    if not (vt == kt or (kt == torch.bfloat16 and vt == torch.float16)):
+        raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE,
+                              f"value cache dtype {vt} with key cache dtype {kt} (same type, or f16 values with bf16 keys)")
+    if cache.k_rot is not None and kt != torch.bfloat16:
+        raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE, "after-cache RoPE is built for a bf16 cache only")
+    if not in_attn and (q_buf is None or q_buf.dtype != kt):
+        raise StreamAttnError(fn, SA_ERR_SHAPE_CODE,
+                              f"q_buf must have the key cache's dtype {kt}, got {None if q_buf is None else q_buf.dtype}")
+    if out.dtype != torch.bfloat16:
+        raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE, f"out must be bfloat16, got {out.dtype}")
+
+
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
                                rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None,
@@ -359,19 +405,17 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
     workspace (attn_workspace): lets the attention run balanced when its grid would leave CU
     slots idle. Returns the visible length used.
     """
+    in_attn = (query_in_attention and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
+               cache.v.dtype == torch.bfloat16)
+    _check_step_dtypes(cache, q_in, k_in, v_in, q_buf, out, in_attn)
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
     after = cache.k_rot is not None
-    if after and cache.k.dtype != torch.bfloat16:
-        raise StreamAttnError("stream_self_attention_step", SA_ERR_UNSUPPORTED_CODE,
-                              "after-cache RoPE is built for a bf16 cache only")
     q_angles = angles[visible - cache.chunk_len:visible] if after else angles
     flag = SA_ROPE_AFTER_CACHE if after else 0
     rope = rope_style != SA_ROPE_NONE
     style = (rope_style | flag) if rope else SA_ROPE_NONE
     bstride = S * cache.Hkv * cache.d
-    in_attn = (query_in_attention and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
-               cache.v.dtype == torch.bfloat16 and q_in.dtype == torch.bfloat16)
     if in_attn:
         qk_norm_rope_v(k_in, cache.k[:, slot:], v_in, cache.v[:, slot:], gamma_k, q_angles if rope else None, eps,
                        norm_scope, style, rope_cs_out=cache.rope_cs if rope else None, k_out_bstride=bstride,
@@ -381,8 +425,8 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
                        norm_scope, style, k_out_bstride=bstride, v_out_bstride=bstride, q_in=q_in, q_out=q_buf,
                        gamma_q=gamma_q)
     else:
-        qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles, eps,
-                     norm_scope, rope_style | flag, k_out_bstride=bstride)
+        qk_norm_rope(q_in, q_buf, k_in, cache.k[:, slot:], gamma_q, gamma_k, q_angles if rope else None, eps,
+                     norm_scope, style, k_out_bstride=bstride)
         kv_cache_append(None, v_in, None, cache.v, chunk_idx, cache.sink_size, cache.window_size)
     keys = cache.k
     if after:

@@ -266,3 +266,92 @@ def test_binding_qk_norm_rope_v_requires_one_output_dtype():
         binding.qk_norm_rope_v(k, torch.empty_like(k), v, torch.empty_like(v), q_in=q,
                                q_out=torch.empty_like(q, dtype=torch.float8_e4m3fn))
     assert e.value.status == binding.SA_ERR_SHAPE_CODE
+
+
+def test_binding_qk_norm_rope_requires_one_output_dtype():
+    """qk_norm_rope writes query and key rows with one output type (the C call takes a single
+    out_dtype): a key output of another type would be written with the query output's element
+    size, so the binding rejects it before any library call; non-bf16 inputs are rejected too."""
+    import torch
+    from head_attention_streaming_amd import binding
+    q = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    k = torch.zeros_like(q)
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.qk_norm_rope(q, torch.empty_like(q), k, torch.empty_like(k, dtype=torch.float8_e4m3fn))
+    assert e.value.status == binding.SA_ERR_SHAPE_CODE
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.qk_norm_rope(q.half(), torch.empty_like(q), k, torch.empty_like(k))
+    assert e.value.status == binding.SA_ERR_UNSUPPORTED_CODE
+
+
+class _RecordingLib:
+    """Stands in for the loaded library: records each entry point's arguments and returns 0."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def fn(*args):
+            self.calls.append((name, args))
+            return 0
+        return fn
+
+
+def test_binding_kv_cache_append_one_call_per_type_pair(monkeypatch):
+    """A bf16 key cache with an f16 value cache: one C call converts both tensors with a single
+    (source, cache) type pair, so the binding issues one call per tensor, each with its own pair
+    (the key copy must not be converted to f16, nor a 2-byte row be copied into an FP8 cache)."""
+    import torch
+    from head_attention_streaming_amd import binding
+    rec = _RecordingLib()
+    monkeypatch.setattr(binding, "lib", lambda: rec)
+    monkeypatch.setattr(binding, "_stream", lambda t=None: None)
+    k = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    ck = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    cv = torch.zeros((1, 8, 2, 64), dtype=torch.float16)
+    binding.kv_cache_append(k, v, ck, cv, 0, 0, 8)
+    names = [c[0] for c in rec.calls]
+    assert names == ["kv_cache_append", "kv_cache_append_ex"]
+    kargs, vargs = rec.calls[0][1], rec.calls[1][1]
+    assert kargs[0] == k.data_ptr() and kargs[1] is None and kargs[2] == ck.data_ptr() and kargs[3] is None
+    assert vargs[0] is None and vargs[1] == v.data_ptr() and vargs[3] == cv.data_ptr()
+    assert vargs[-3:-1] == (binding.SA_DTYPE_BF16, binding.SA_DTYPE_F16)
+    # FP8 key cache, bf16 value cache: the key rows are rounded to E4M3, the values byte-copied
+    rec.calls.clear()
+    ck8 = torch.zeros((1, 8, 2, 64), dtype=torch.float8_e4m3fn)
+    binding.kv_cache_append(k, v, ck8, ck, 0, 0, 8)
+    assert [c[0] for c in rec.calls] == ["kv_cache_append_ex", "kv_cache_append"]
+    assert rec.calls[0][1][-3:-1] == (binding.SA_DTYPE_BF16, binding.SA_DTYPE_FP8_E4M3)
+    # same types: one call for both
+    rec.calls.clear()
+    binding.kv_cache_append(k, v, ck, torch.zeros_like(ck), 0, 0, 8)
+    assert [c[0] for c in rec.calls] == ["kv_cache_append"]
+
+
+@pytest.mark.parametrize("kdt,vdt,qdt,code", [
+    ("float8_e4m3fn", "float16", "float8_e4m3fn", -3),   # FP8 keys with 16-bit values: not built
+    ("float8_e4m3fn", "bfloat16", "float8_e4m3fn", -3),
+    ("bfloat16", "bfloat16", "float8_e4m3fn", -2),      # queries buffered in another type
+    ("bfloat16", "float16", "float16", -2),
+    ("float16", "float16", "float16", -3),              # f16 key cache: not built
+])
+def test_binding_streaming_step_rejects_unbuilt_dtype_combinations(kdt, vdt, qdt, code, monkeypatch):
+    """The streaming step checks the (key cache, value cache, query buffer) types before its first
+    launch, so no kernel ever writes rows of one type at another type's element size."""
+    import torch
+    from head_attention_streaming_amd import binding
+    rec = _RecordingLib()
+    monkeypatch.setattr(binding, "lib", lambda: rec)
+    B, Lc, H, d = 1, 4, 2, 64
+    cache = binding.BlockKVCache(B, H, d, Lc, 0, 2 * Lc, dtype=getattr(torch, kdt), device="cpu",
+                                 v_dtype=getattr(torch, vdt))
+    x = torch.zeros((B, Lc, H, d), dtype=torch.bfloat16)
+    q_buf = torch.zeros((B, Lc, H, d), dtype=getattr(torch, qdt))
+    out = torch.zeros((B, Lc, H, d), dtype=torch.bfloat16)
+    g = torch.ones(d)
+    ang = torch.zeros((Lc, d // 2))
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.stream_self_attention_step(cache, 0, x, x, x, q_buf, out, g, g, ang, 1e-6, 0.125)
+    assert e.value.status == code
+    assert rec.calls == [] and cache._current is None  # nothing launched, no chunk opened
