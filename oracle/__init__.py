@@ -140,9 +140,13 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Spacing of ``dtype`` values at the magnitude of x (the quantum used by round_to)."""
+    """Spacing of ``dtype`` values at the magnitude of x (the quantum used by round_to): in the
+    binade [2^(e-1), 2^e) of x the p significant bits are 2^(e-p) apart; at and below the smallest
+    normal 2^emin (zero included) the subnormals are 2^(emin-p+1) apart."""
     p, emin, _ = _FORMATS[dtype]
-    _, e = np.frexp(np.asarray(x, dtype=np.float64))
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.where(x == 0, emin, e)   # frexp(0) gives exponent 0, which is not zero's binade
     return np.ldexp(1.0, np.maximum(e - p, emin - p + 1))
 
 

@@ -449,3 +449,54 @@ def test_round_to_e4m3_matches_the_format_and_torch():
     ours = oracle.round_to(vals.astype(np.float64), "e4m3")
     ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------ ulp (the tolerance quantum)
+
+@pytest.mark.parametrize("dtype,x,spacing", [
+    # bf16: 8 significant bits. Binade [1, 2) has spacing 2^-7, [2, 4) 2^-6, [0.5, 1) 2^-8;
+    # below the smallest normal 2^-126 the spacing stays 2^-133 (subnormals)
+    ("bf16", 1.0, 2.0 ** -7), ("bf16", 1.999, 2.0 ** -7), ("bf16", 2.0, 2.0 ** -6), ("bf16", 0.75, 2.0 ** -8),
+    ("bf16", -3.0, 2.0 ** -6), ("bf16", 2.0 ** -126, 2.0 ** -133), ("bf16", 2.0 ** -130, 2.0 ** -133),
+    ("bf16", 0.0, 2.0 ** -133), ("bf16", 5.0, 2.0 ** -5),
+    # f16: 11 significant bits, smallest normal 2^-14, largest finite 65504 = (2 - 2^-10) 2^15
+    ("f16", 1.0, 2.0 ** -10), ("f16", 65504.0, 32.0), ("f16", 2.0 ** -14, 2.0 ** -24),
+    ("f16", 2.0 ** -20, 2.0 ** -24), ("f16", 0.0, 2.0 ** -24), ("f16", 1000.0, 0.5),
+    # E4M3: 4 significant bits, smallest normal 2^-6, largest finite 448 = 1.75 * 2^8
+    ("e4m3", 1.0, 2.0 ** -3), ("e4m3", 448.0, 32.0), ("e4m3", 2.0 ** -6, 2.0 ** -9),
+    ("e4m3", 2.0 ** -8, 2.0 ** -9), ("e4m3", 0.0, 2.0 ** -9), ("e4m3", 20.0, 2.0),
+])
+def test_ulp_hand_derived_spacings(dtype, x, spacing):
+    """Spacings worked out by hand from each format's significand width and smallest normal
+    exponent (the formats' definitions), not from the oracle's expression."""
+    assert oracle.ulp(np.array([x]), dtype)[0] == spacing
+
+
+@pytest.mark.parametrize("dtype,tdt,idt,lo,hi", [
+    ("bf16", torch.bfloat16, torch.int16, -133, 127),
+    ("f16", torch.float16, torch.int16, -24, 15),
+    ("e4m3", torch.float8_e4m3fn, torch.uint8, -9, 8),
+])
+def test_ulp_equals_gap_to_next_bit_pattern(dtype, tdt, idt, lo, hi):
+    """For 10^5 magnitudes spread over the format's whole range (subnormals included), ulp(x)
+    equals the gap between the largest representable value <= x and the value of the next bit
+    pattern, both decoded by torch: positive encodings are ordered like their values, so the next
+    pattern is the next representable number."""
+    rng = np.random.default_rng(7)
+    x = np.exp2(rng.uniform(lo, hi + 0.999, size=100_000))
+    x = x[x < {"bf16": 3.3e38, "f16": 65504.0, "e4m3": 448.0}[dtype]]
+    bits = torch.from_numpy(x).to(tdt).view(idt).to(torch.int64)
+
+    def val(b):
+        return b.to(idt).view(tdt).to(torch.float64).numpy()
+
+    xt = torch.from_numpy(x)
+    # step the encoding to the largest value <= x (the conversion may have rounded up, or, for
+    # bf16 via fp32, twice down)
+    for _ in range(3):
+        bits = torch.where(torch.from_numpy(val(bits)) > xt, bits - 1, bits)
+        bits = torch.where(torch.from_numpy(val(bits + 1)) <= xt, bits + 1, bits)
+    below, above = val(bits), val(bits + 1)
+    assert (below <= x).all() and (above > x).all()
+    np.testing.assert_array_equal(oracle.ulp(x, dtype), above - below)
+    np.testing.assert_array_equal(oracle.ulp(-x, dtype), above - below)
