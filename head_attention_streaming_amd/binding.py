@@ -21,8 +21,8 @@ SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2,
 
 EXPORTS = ("qk_norm_rope", "qk_norm_rope_ex", "qk_norm_rope_v", "kv_cache_slot", "kv_cache_positions", "kv_cache_append",
            "kv_cache_append_ex", "kv_cache_rope", "attn_forward", "attn_forward_f16", "attn_forward_kvstride",
-           "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "attn_forward_qnorm",
-           "sa_last_error")
+           "attn_forward_window", "attn_forward_workspace_bytes", "attn_forward_ws", "attn_forward_ws_static",
+           "attn_forward_qnorm", "sa_last_error")
 
 _lib = None
 
@@ -60,6 +60,7 @@ def lib():
         L.attn_forward_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
         L.attn_forward_workspace_bytes.argtypes = [I]
         L.attn_forward_ws.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
+        L.attn_forward_ws_static.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, I64, I, P]
         L.attn_forward_qnorm.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, I, F, I, I, I64, I, P, I64, P]
         L.sa_last_error.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
@@ -163,6 +164,19 @@ def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None
            lib().attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
                                  d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
+    return out
+
+
+def attn_forward_ws_static(q, k, v, out, scale: float, Lk: int | None = None, window=(-1, -1)):
+    """attn_forward_ws with the library's own per-GPU scratch instead of a workspace: allocates
+    nothing. Calls that overlap on one GPU race (they share that scratch)."""
+    B, Lq, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    left, right = (int(x) for x in window)
+    _check("attn_forward_ws_static",
+           lib().attn_forward_ws_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq,
+                                        S if Lk is None else int(Lk), d, float(scale), left, right, S * Hkv * d,
+                                        _attn_dtype(q, k, v), _stream(q)))
     return out
 
 

@@ -20,6 +20,7 @@
 //   * exp2 with log2(e) folded into the scale; the output is divided by l once at the end.
 // Probabilities use f16 (11-bit significand) for the P*V product; bf16 V is converted to f16
 // when it is staged into LDS (exact for |v| in [2^-17, 65504]).
+#include <mutex>
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -908,9 +909,19 @@ __global__ void __launch_bounds__(NW * 64) attn_merge_kernel(KParams p) {
 constexpr int kBalancedWaves = 8;
 
 // Workspace of a balanced launch: two partial slots per workgroup, one per wave and lane.
-int64_t balanced_workspace_bytes(int d, int wgs) {
+constexpr int64_t balanced_workspace_bytes(int d, int wgs) {
     return (int64_t)2 * wgs * kBalancedWaves * 64 * (2 * (d / 32) + 1) * (int64_t)sizeof(u32x4);
 }
+
+// Library-held partial results for callers that cannot allocate device memory: one array per
+// GPU (each device's copy of this code object holds its own), kept until the process ends. It
+// covers a balanced launch at the largest head dim built (d = 128) with one persistent
+// workgroup per CU on up to 256 CUs (MI355X): 37.7 MB. Its contents persist from call to call;
+// a balanced launch writes every partial before it reads it, so nothing needs clearing.
+constexpr int kScratchMaxCUs = 256;
+constexpr int64_t kScratchBytes = balanced_workspace_bytes(128, kScratchMaxCUs);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kScratchMaxDevices = 64;
 
 // A balanced launch pays when the grid's rounds would keep the slots under 90 % busy, for
 // full-range attention (every unit the same number of key tiles), more units than slots and key
@@ -1036,6 +1047,29 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 int64_t attn_workspace_bytes(int d) { return balanced_workspace_bytes(d, device_cu_count()); }
+
+int64_t attn_scratch_bytes() { return kScratchBytes; }
+
+// Device address of the current GPU's scratch array, looked up once per device with that device
+// current. Host code uses only this address: the array's own name is a host-side stand-in.
+hipError_t attn_scratch(void** out) {
+    static std::mutex mu;
+    static void* addr[kScratchMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 128) {

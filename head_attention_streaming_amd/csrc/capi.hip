@@ -161,6 +161,25 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out, int 
                     workspace, workspace_bytes);
 }
 
+int attn_forward_ws_static(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int Lq,
+                           int Lk, int d, float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                           void* stream) {
+    // same validation as attn_forward_ws first, so bad arguments never touch the scratch array
+    const int st = check_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype);
+    if (st < 0) return st;
+    if (st > 0) return ok();
+    const int64_t need = sa::attn_workspace_bytes(d);
+    if (need > sa::attn_scratch_bytes())
+        return fail(SA_ERR_UNSUPPORTED, "attn_forward_ws_static: this device needs %lld bytes of partial-result scratch, "
+                    "the library holds %lld (one workgroup per CU on up to 256 CUs)", (long long)need,
+                    (long long)sa::attn_scratch_bytes());
+    void* ptr = nullptr;
+    const hipError_t e = sa::attn_scratch(&ptr);
+    if (e != hipSuccess) return hip_status(e, "attn_forward_ws_static: scratch address");
+    return run_attn(q, k, v, out, B, Hq, Hkv, Lq, Lk, d, scale, window_left, window_right, kv_bstride, dtype, stream,
+                    ptr, sa::attn_scratch_bytes());
+}
+
 int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, const float* gamma_q, float eps,
                        const float* rope_cs, int rope_style, int B, int Hq, int Hkv, int Lq, int Lk, int d,
                        float scale, int window_left, int window_right, int64_t kv_bstride, int dtype, void* workspace,

@@ -76,6 +76,8 @@ struct CopyArgs {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 int64_t attn_workspace_bytes(int d);  // workspace that lets every shape of this device run balanced
+int64_t attn_scratch_bytes();          // size of the library-held scratch array (per GPU)
+hipError_t attn_scratch(void** out);   // its device address on the current GPU
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 hipError_t launch_copy_rows(const CopyArgs& a, hipStream_t stream);
 

@@ -19,7 +19,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
  *     enqueues kernels on that stream and returns; none synchronises.
  *   - Ownership: the caller allocates and frees every buffer, including the K/V cache. The
- *     library allocates no device memory and keeps no pointer after a call returns.
+ *     library allocates no device memory at run time and keeps no caller pointer after a call
+ *     returns; its only device memory is the scratch array of attn_forward_ws_static, part of
+ *     its loaded code object.
  *   - Errors: arguments are validated on the host before anything is launched. A negative
  *     status means nothing was enqueued by that call (except SA_ERR_HIP, which reports a failed
  *     launch). sa_last_error() returns a thread-local text for the last failing call.
@@ -311,6 +313,25 @@ int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
                     int B, int Hq, int Hkv, int Lq, int Lk, int d,
                     float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_forward_ws_static -- attn_forward_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). This call allocates nothing: the partial results of a balanced launch go
+ * to a scratch array the library holds in device memory, one per GPU (its address is looked up
+ * on the first call on each device and kept), sized for one persistent workgroup per CU on up
+ * to 256 CUs at d = 128 (37.7 MB; attn_forward_workspace_bytes(d) of an MI355X). A device that
+ * would need more returns SA_ERR_UNSUPPORTED before anything is launched.
+ * Operation, arguments, results and errors otherwise as attn_forward_ws with a workspace of
+ * that size: the same kernels, so the same bits. Every call on one GPU shares that GPU's array
+ * (it keeps the last call's partials; nothing needs clearing), so calls that overlap on one GPU
+ * -- on different streams or host threads -- race; serialise them. The stream must belong to the
+ * current device.
+ */
+int attn_forward_ws_static(const void* q, const void* k, const void* v, void* out,
+                           int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                           float scale, int window_left, int window_right, int64_t kv_bstride, int dtype,
+                           void* stream);
 
 /*
  * attn_forward_qnorm -- attn_forward_ws with the query prologue fused into the attention: each
