@@ -141,12 +141,16 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         info["v_cache_dtype"] = w.v_cache_dtype
     g = torch.Generator().manual_seed(w.seed)
     gq, gk = synthetic.norm_weight(w.d, g).to(dev), synthetic.norm_weight(w.d, g).to(dev)
-    nsets = 6  # rotate input sets (6 x 55 MB) so the prologue and append are not served from cache
+    # Rotating input sets (10 x 55 MB) and query buffers (4 x 18 MB): together with the two cache
+    # tensors (2 x 73 MB) each HBM-bound step cycles over ~770 MB of distinct bytes, three times
+    # the 256 MB Infinity Cache, so no input or output of a timed call is still cache-resident.
+    nsets, nbufs = 10, 4
     sets = []
     for i in range(nsets):
         gi = torch.Generator().manual_seed(w.seed + i)
         sets.append([synthetic.normal((w.B, Lc, w.Hq, w.d), "bf16", gi).to(dev) for _ in range(3)])
-    q_buf = torch.empty((w.B, Lc, w.Hq, w.d), dtype=cdt, device=dev)
+    q_bufs = [torch.empty((w.B, Lc, w.Hq, w.d), dtype=cdt, device=dev) for _ in range(nbufs)]
+    q_buf = q_bufs[0]
     out = torch.empty((w.B, Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
     state = {"c": 0}
     if after:  # rows 0 .. visible-1 of the visible sequence (visible = S once the cache is full)
@@ -181,9 +185,16 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         else:
             binding.attn_forward_kvstride(q_buf, keys, cache.v, out, S, w.scale, False)
 
-    # the HBM-bound steps alone, on rotating input sets (each set is read once per 6 calls)
+    # the HBM-bound steps alone, on rotating input sets, query buffers and cache slots (each input
+    # set is read once per 10 calls; outputs go to one of 4 query buffers and one of the cache's
+    # S / Lc chunk slots)
     rot = {"i": 0}
-    slot = cache.slot_base
+    nslots = S // Lc
+
+    def next_set():
+        i = rot["i"]
+        rot["i"] = i + 1
+        return sets[i % nsets], q_bufs[i % nbufs], (i % nslots) * Lc
 
     q_ang = angles[7][S - Lc:] if after else angles[0]
     flag = binding.SA_ROPE_AFTER_CACHE if after else 0
@@ -191,23 +202,20 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
     gk_in = synthetic.norm_weight(w.Hkv * w.d, g).to(dev)
 
     def prologue(scope=binding.SA_NORM_HEAD):
-        q, k, _ = sets[rot["i"] % nsets]
-        rot["i"] += 1
+        (q, k, _), qb, slot = next_set()
         inner = scope == binding.SA_NORM_INNER
-        binding.qk_norm_rope(q, q_buf, k, cache.k[:, slot:], gq_in if inner else gq, gk_in if inner else gk, q_ang,
+        binding.qk_norm_rope(q, qb, k, cache.k[:, slot:], gq_in if inner else gq, gk_in if inner else gk, q_ang,
                              1e-6, scope, binding.SA_ROPE_SPLIT | flag, k_out_bstride=S * w.Hkv * w.d)
 
     def append():
-        _, _, v = sets[rot["i"] % nsets]
-        rot["i"] += 1
-        binding.kv_cache_append(None, v, None, cache.v, state["c"], 0, S)
+        (_, _, v), _, slot = next_set()
+        binding.kv_cache_append(None, v, None, cache.v, slot // Lc, 0, S)
 
     def prologue_v():  # the one-launch prologue: queries, keys and values
-        q, k, v = sets[rot["i"] % nsets]
-        rot["i"] += 1
+        (q, k, v), qb, slot = next_set()
         binding.qk_norm_rope_v(k, cache.k[:, slot:], v, cache.v[:, slot:], gk, q_ang, 1e-6, binding.SA_NORM_HEAD,
                                binding.SA_ROPE_SPLIT | flag, k_out_bstride=S * w.Hkv * w.d,
-                               v_out_bstride=S * w.Hkv * w.d, q_in=q, q_out=q_buf, gamma_q=gq)
+                               v_out_bstride=S * w.Hkv * w.d, q_in=q, q_out=qb, gamma_q=gq)
 
     elem = 2 * w.B * Lc * w.Hq * w.d  # bytes of one [B, Lc, H, d] bf16 tensor
     out_elem = elem // 2 if w.cache_dtype == "e4m3" else elem   # the same tensor in the cache type
@@ -293,6 +301,46 @@ def time_loop(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
+def shader_clock_mhz(fn, seconds: float = 1.0):
+    """Shader clock under the step's own load: runs `fn` back to back for about `seconds` while
+    one `amd-smi metric -c` call reads the current clock of every XCD; returns (mean, min, max)
+    in MHz, or None when the tool is missing or reports nothing. Called after the timed region,
+    so it never perturbs the timing."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    box = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run([tool, "metric", "-c"], capture_output=True, text=True, timeout=20)
+            box["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            box["text"] = ""
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()  # keep the host within a few steps of the GPU
+    torch.cuda.synchronize()
+    clk = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", box.get("text", ""))]
+    if not clk:
+        return None
+    return round(sum(clk) / len(clk), 1), min(clk), max(clk)
+
+
 def cpu_baseline(w, tensors, target_s: float):
     """The fp64 oracle on a bounded row sample of the same inputs; returns a dict."""
     import numpy as np
@@ -329,10 +377,13 @@ def cpu_baseline(w, tensors, target_s: float):
         rows, t = run(n_full)
     # flops of the sampled rows: 4*d per visible key of each row
     fl = 4.0 * w.d * float(visible_keys(w, (rows // w.Hq) % w.Lq).sum())
+    full = workload_flops(w)
     return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {total} query rows (random, seed 0), each over all its keys; "
                       f"{t:.1f} s wall, fp64, {threads} threads",
-            "seconds": round(t, 2)}
+            "seconds": round(t, 2),
+            # the whole problem at the sample's rate (every row costs 4*d flops per visible key)
+            "full_problem_seconds_extrapolated": round(t * full / fl, 1)}
 
 
 def main():
@@ -356,6 +407,7 @@ def main():
     ms_step, wall_ms = time_loop(step, args.steps, 0)
     ms_kern, _ = time_loop(kern, args.steps, 2) if kern is not step else (ms_step, wall_ms)
 
+    clock = shader_clock_mhz(kern)
     hbm = {}
     for name, (fn, nbytes) in info.pop("hbm_steps", {}).items():
         ms_h, _ = time_loop(fn, args.steps, args.warmup)
@@ -384,7 +436,11 @@ def main():
         "dtype": "e4m3" if fp8 else w.dtype,
         "data": "synthetic",
         "config": dict(info, flops_per_step=flops, pct_of_bf16_peak=round(100 * value / PEAK_MFMA_16BIT, 2),
-                       wall_ms_per_step=round(wall_ms, 4)),
+                       wall_ms_per_step=round(wall_ms, 4),
+                       shader_clock_mhz=None if clock is None else
+                       {"mean": clock[0], "min": clock[1], "max": clock[2],
+                        "how": "amd-smi metric -c, every XCD, read while the kernel ran back to back "
+                               "right after the timed steps"}),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": f"attn_fwd_kernel<{w.d},{'e4m3' if fp8 else w.dtype}>",

@@ -71,3 +71,9 @@ def test_cpu_baseline_reports_the_oracle_on_a_row_sample():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "query rows" in r["sample"]
+    # the whole problem at the sample's rate, labelled as an extrapolation
+    sampled = int(r["sample"].split(" of ")[0])
+    total = w.B * w.Lq * w.Hq
+    assert r["full_problem_seconds_extrapolated"] >= r["seconds"] * 0.99 * min(1.0, total / sampled) - 0.05
+    if sampled == total:
+        assert abs(r["full_problem_seconds_extrapolated"] - r["seconds"]) <= 0.1
