@@ -72,6 +72,8 @@ def _load():
         lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I]
         lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I]
         lib.oracle_attention.restype = I
+        lib.oracle_attention_spread.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I, P, P, P]
+        lib.oracle_attention_spread.restype = I
         _lib = lib
     return _lib
 
@@ -224,3 +226,37 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
     if rc != 0:
         raise RuntimeError("oracle_attention failed")
     return out if rows is not None else out.reshape(B, Lq, Hq, d)
+
+
+def attention_spread(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
+                     rows: np.ndarray | None = None, nthreads: int | None = None,
+                     window: tuple[int, int] | None = None):
+    """``attention`` plus what a tolerance for rounded softmax weights needs, from the exact
+    weights w_j = softmax(s)_j of each row: A = sum_j w_j |v_j - o| and R = sqrt(sum_j w_j^2
+    (v_j - o)^2) per output element (same shape as the output), and the row's score range
+    max_j s_j - min_j s_j in base-2 exponent units (shape: the output without its last axis).
+    Returns (o, A, R, span)."""
+    if window is not None and causal:
+        raise ValueError("give either causal or window")
+    win_left, win_right = window if window is not None else ((-1, 0) if causal else (-1, -1))
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Lq, Hq, d = q.shape
+    assert v.shape == k.shape and k.shape[0] == B and k.shape[3] == d and Hq % k.shape[2] == 0
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = B * Lq * Hq if rows is None else rows_arr.size
+    out = np.empty((nrows, d))
+    a = np.empty((nrows, d))
+    r = np.empty((nrows, d))
+    span = np.empty((nrows,))
+    rc = _load().oracle_attention_spread(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                         None if rows_arr is None else _ptr(rows_arr), nrows, B, Hq, k.shape[2],
+                                         Lq, k.shape[1], d, float(scale), int(win_left), int(win_right),
+                                         nthreads or default_threads(), _ptr(a), _ptr(r), _ptr(span))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_spread failed")
+    if rows is None:
+        return (out.reshape(B, Lq, Hq, d), a.reshape(B, Lq, Hq, d), r.reshape(B, Lq, Hq, d),
+                span.reshape(B, Lq, Hq))
+    return out, a, r, span

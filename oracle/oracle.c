@@ -133,6 +133,11 @@ typedef struct {
     int64_t win_left, win_right; /* visible keys of query i: [i+s-win_left, i+s+win_right], s = Lk-Lq; <0 = unbounded */
     double scale;
     int tid, nthreads;
+    /* optional per-row outputs (NULL: not computed), for tolerances of kernels that round the
+     * softmax weights: spread_a[n*d + t] = sum_j w_j |v_jt - o_t| and spread_r[n*d + t] =
+     * sqrt(sum_j w_j^2 (v_jt - o_t)^2) with w_j = p_j / l the exact weights; span[n] = the range
+     * of the row's visible scores, max_j s_j - min_j s_j, in base-2 exponent units (times log2 e) */
+    double *spread_a, *spread_r, *span;
 } attn_job;
 
 /* One query row: s_j = scale * <q_i, k_j> for every visible key j, then
@@ -172,6 +177,26 @@ static void attention_row(const attn_job* J, int64_t row, double* scores, double
         for (int t = 0; t < d; ++t) o[t] += scores[n] * vj[t];
     }
     for (int t = 0; t < d; ++t) o[t] = o[t] / l;
+    if (J->spread_a) {
+        const int64_t n_out = o - J->out;   /* this row's offset into the outputs */
+        double* a = J->spread_a + n_out;
+        double* r = J->spread_r + n_out;
+        for (int t = 0; t < d; ++t) a[t] = r[t] = 0.0;
+        double smin = INFINITY;
+        for (int64_t n = 0; n < nvis; ++n) {
+            const double w = scores[n] / l;
+            const double* vj = J->v + (((int64_t)b * J->Lk + jlo + n) * J->Hkv + hk) * d;
+            for (int t = 0; t < d; ++t) {
+                const double dev = vj[t] - o[t];
+                a[t] += w * fabs(dev);
+                r[t] += (w * dev) * (w * dev);
+            }
+            /* scores[n] holds exp(s_n - m): the smallest gives the row's score range */
+            if (scores[n] < smin) smin = scores[n];
+        }
+        for (int t = 0; t < d; ++t) r[t] = sqrt(r[t]);
+        J->span[n_out / d] = nvis > 0 ? -log2(smin) : 0.0;
+    }
 }
 
 static void* attention_worker(void* arg) {
@@ -191,9 +216,34 @@ static void* attention_worker(void* arg) {
  * all keys; (-1, 0): causal). out: [nrows, d], row n is the attention output of query row rows[n]
  * (flat index (b * Lq + i) * Hq + h), or of row n when rows is NULL (then nrows = B*Lq*Hq).
  * Returns 0 on success, -1 on invalid arguments or allocation failure. */
+static int run_attention(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
+                         int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
+                         int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
+                         double* span);
+
 int oracle_attention(const double* q, const double* k, const double* v, double* out,
                      const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
                      double scale, int64_t win_left, int64_t win_right, int nthreads) {
+    return run_attention(q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, nthreads,
+                         NULL, NULL, NULL);
+}
+
+/* oracle_attention plus, per output element, the spread of V under the exact softmax weights
+ * (spread_a, spread_r: [nrows, d]) and, per row, the range of its scores in base-2 units (span:
+ * [nrows]); see attn_job. Same return values. */
+int oracle_attention_spread(const double* q, const double* k, const double* v, double* out,
+                            const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                            double scale, int64_t win_left, int64_t win_right, int nthreads, double* spread_a,
+                            double* spread_r, double* span) {
+    if (!spread_a || !spread_r || !span) return -1;
+    return run_attention(q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, nthreads,
+                         spread_a, spread_r, span);
+}
+
+static int run_attention(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
+                         int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
+                         int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
+                         double* span) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq < 0 || Lk < 0 || d <= 0) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -202,7 +252,8 @@ int oracle_attention(const double* q, const double* k, const double* v, double* 
     int created[256];
     int rc = 0;
     for (int t = 0; t < nthreads; ++t) {
-        attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, win_left, win_right, scale, t, nthreads};
+        attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, win_left, win_right, scale, t, nthreads,
+                      spread_a, spread_r, span};
         jobs[t] = J;
         created[t] = 0;
     }

@@ -16,6 +16,10 @@ void oracle_rope(const double* z, const double* angles, double* out, int B, int 
 int oracle_attention(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
                      int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale, int64_t win_left,
                      int64_t win_right, int nthreads);
+int oracle_attention_spread(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
+                            int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
+                            int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
+                            double* span);
 
 static int fails = 0;
 #define CHECK(c)                                                             \
@@ -123,6 +127,15 @@ int main(void) {
     CHECK(oracle_attention(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, 2, 1, 3) == 0);
     for (int n = 0; n < 3; ++n) CHECK(memcmp(sub + n * AD, out + rows[n] * AD, AD * sizeof(double)) == 0);
     CHECK(oracle_attention(q, k, v, out, NULL, 0, AB, 3, 2, LQ, LK, AD, 0.25, -1, -1, 1) == -1);
+    /* spreads over a row subset, threaded: a single visible key (window (0, 0)) has none */
+    double *sa = malloc(sizeof(double) * 3 * AD), *sr = malloc(sizeof(double) * 3 * AD), span[3];
+    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, 0, 0, 2, sa, sr, span) == 0);
+    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] == 0.0 && sr[i] == 0.0);
+    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, -1, -1, 3, sa, sr, span) == 0);
+    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] > 0.0 && sr[i] > 0.0 && sr[i] <= sa[i]);
+    for (int i = 0; i < 3; ++i) CHECK(span[i] > 0.0);
+    free(sa);
+    free(sr);
     free(q);
     free(k);
     free(v);

@@ -500,3 +500,57 @@ def test_ulp_equals_gap_to_next_bit_pattern(dtype, tdt, idt, lo, hi):
     assert (below <= x).all() and (above > x).all()
     np.testing.assert_array_equal(oracle.ulp(x, dtype), above - below)
     np.testing.assert_array_equal(oracle.ulp(-x, dtype), above - below)
+
+
+# ------------------------------------------------------------------ spread of V under the weights
+
+def test_attention_spread_single_key_is_zero():
+    """One visible key: weight 1, o = v, so both spreads and the score range are exactly 0."""
+    q, k, v = _rand(1, 3, 2, 8), _rand(1, 1, 2, 8), _rand(1, 1, 2, 8)
+    o, a, r, span = oracle.attention_spread(q, k, v, 0.3)
+    assert np.array_equal(o, np.broadcast_to(v, o.shape))
+    assert not a.any() and not r.any() and not span.any()
+
+
+def test_attention_spread_uniform_weights_closed_form():
+    """q = 0: every weight is 1/N, so o = mean(V), A = mean |v - mean| and R = sqrt(sum (v - mean)^2) / N,
+    computed here from V alone; the score range is 0."""
+    B, Lq, Lk, H, d = 2, 3, 37, 2, 16
+    q, k, v = np.zeros((B, Lq, H, d)), _rand(B, Lk, H, d), _rand(B, Lk, H, d)
+    o, a, r, span = oracle.attention_spread(q, k, v, 0.7)
+    mean = v.mean(axis=1, keepdims=True)                       # [B, 1, H, d]
+    np.testing.assert_allclose(o, np.broadcast_to(mean, o.shape), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(a, np.broadcast_to(np.abs(v - mean).mean(axis=1, keepdims=True), a.shape),
+                               rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r, np.broadcast_to(np.sqrt(((v - mean) ** 2).sum(axis=1, keepdims=True)) / Lk,
+                                                  r.shape), rtol=1e-12, atol=1e-15)
+    assert not span.any()
+
+
+def test_attention_spread_two_keys_hand_worked():
+    """Two keys with score gap ln 3 (weights 3/4, 1/4): v0 - o = w1 (v0 - v1), v1 - o = w0 (v1 - v0),
+    so A = 2 w0 w1 |v0 - v1| = (3/8)|v0 - v1|, R = sqrt(2) w0 w1 |v0 - v1| = (3 sqrt(2)/16)|v0 - v1|,
+    and the score range is log2(3)."""
+    q = np.array([[[[math.log(3.0), 0.0]]]])
+    k = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])
+    v = np.array([[[[4.0, 8.0]], [[0.0, -4.0]]]])
+    o, a, r, span = oracle.attention_spread(q, k, v, 1.0)
+    dv = np.array([4.0, 12.0])
+    np.testing.assert_allclose(o[0, 0, 0], [3.0, 5.0], rtol=1e-14)
+    np.testing.assert_allclose(a[0, 0, 0], 3.0 / 8.0 * dv, rtol=1e-13)
+    np.testing.assert_allclose(r[0, 0, 0], 3.0 * math.sqrt(2.0) / 16.0 * dv, rtol=1e-13)
+    np.testing.assert_allclose(span[0, 0, 0], math.log2(3.0), rtol=1e-13)
+
+
+def test_attention_spread_rows_and_windows_match_full():
+    """Row subsets and windowed rows give the same o as ``attention`` and the same spreads as the
+    full computation."""
+    q, k, v = _rand(2, 9, 4, 8), _rand(2, 13, 2, 8), _rand(2, 13, 2, 8)
+    o, a, r, span = oracle.attention_spread(q, k, v, 0.5, window=(3, 1))
+    np.testing.assert_array_equal(o, oracle.attention(q, k, v, 0.5, window=(3, 1)))
+    rows = np.array([5, 0, 71, 33])
+    o2, a2, r2, s2 = oracle.attention_spread(q, k, v, 0.5, window=(3, 1), rows=rows)
+    np.testing.assert_array_equal(o2, o.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(a2, a.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(r2, r.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(s2, span.reshape(-1)[rows])
