@@ -122,6 +122,38 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         out = torch.empty_like(q)
         ws = binding.attn_workspace(w.d, dev) if use_ws else None
         info["balanced"] = use_ws
+        if w.rope_scope == "after":
+            # after-cache RoPE over a static context: the cache (built once, outside the step)
+            # holds normalised, unrotated keys; each step rotates all of them into k_rot with the
+            # cache-relative angle rows and normalises and rotates the queries (rows after them)
+            gk = synthetic.norm_weight(w.d, g).to(dev)
+            ck, cv, k_rot = torch.empty_like(k), torch.empty_like(v), torch.empty_like(k)
+            binding.context_kv(k, v, ck, cv, gk, 1e-6)
+            ctx_ang = synthetic.rope_angles(np.arange(w.Lk), w.d).to(dev)
+            q_ang = synthetic.rope_angles(np.arange(w.Lk, w.Lk + w.Lq), w.d).to(dev)
+            q_buf = torch.empty_like(q)
+
+            def step():
+                binding.cross_attention_step(ck, cv, q, out, gq, 1e-6, w.scale, q_buf=q_buf, q_angles=q_ang,
+                                             context_angles=ctx_ang, k_rot=k_rot, workspace=ws)
+
+            def kern():
+                binding.attn_forward_ws(q_buf, k_rot, cv, out, w.scale, ws) if ws is not None else \
+                    binding.attn_forward_kvstride(q_buf, k_rot, cv, out, w.Lk, w.scale, False)
+
+            def rot_keys():
+                binding.kv_cache_rope(ck, k_rot, ctx_ang, 0, w.Lk, 0, w.Lk, binding.SA_ROPE_SPLIT)
+
+            def q_prologue():
+                binding.qk_norm_rope(q, q_buf, None, None, gq, None, q_ang, 1e-6, binding.SA_NORM_HEAD,
+                                     binding.SA_ROPE_SPLIT, Hkv=0)
+            kbytes = 2 * w.B * w.Lk * w.Hkv * w.d
+            qbytes = 2 * w.B * w.Lq * w.Hq * w.d
+            info["hbm_steps"] = {"kv_cache_rope": (rot_keys, 2 * kbytes + w.Lk * (w.d // 2) * 4),
+                                 "qk_norm_rope_q": (q_prologue, 2 * qbytes + w.Lq * (w.d // 2) * 4 + w.d * 4)}
+            info["step"] = ("kv_cache_rope(all context keys -> k_rot) + qk_norm_rope(Q) + attention "
+                            "(cross_attention_step, after-cache RoPE)")
+            return w, step, kern, info, (q, k, v)
 
         def kern():  # the Q RMSNorm is fused into the attention kernel's query load
             binding.attn_forward_qnorm(q, k, v, out, w.scale, gq, 1e-6, workspace=ws)

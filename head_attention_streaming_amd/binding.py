@@ -347,14 +347,31 @@ class BlockKVCache:
         self.slot_base = 0
         self.visible_len = 0
         self._current = None
+        self._last = None   # last chunk written in the current stream (None: a fresh stream)
 
     @property
     def capacity(self) -> int:
         return self.sink_size + self.window_size
 
+    def reset(self):
+        """Start a new stream: the next chunk must be chunk 0. The storage keeps its old rows, but
+        none of them is visible again before a chunk of the new stream overwrites it (chunk c
+        sees exactly the rows chunks 0 .. c of its own stream wrote), so nothing is cleared."""
+        if self._current is not None:
+            raise RuntimeError("reset inside before_update / after_update")
+        self.slot_base = self.visible_len = 0
+        self._last = None
+
     def before_update(self, chunk_idx: int):
+        """Chunks of a stream are written in order: chunk 0 (which also restarts a used cache, as
+        reset() does) or the chunk after the last one -- the visible rows are those chunks 0 .. c
+        wrote, so a skipped chunk would expose rows of another stream."""
         if self._current is not None:
             raise RuntimeError("before_update called twice without after_update")
+        expected = 0 if self._last is None else self._last + 1
+        if chunk_idx != 0 and chunk_idx != expected:
+            raise StreamAttnError("before_update", SA_ERR_SHAPE_CODE,
+                                  f"chunk {chunk_idx} after chunk {self._last}: write chunks in order (0 restarts)")
         self.slot_base, self.visible_len = kv_cache_slot(chunk_idx, self.chunk_len, self.sink_size,
                                                          self.window_size)
         self._current = chunk_idx
@@ -368,13 +385,37 @@ class BlockKVCache:
         if self._current != chunk_idx:
             raise RuntimeError("after_update does not match before_update")
         self._current = None
+        self._last = chunk_idx
 
 
-def _check_step_dtypes(cache: BlockKVCache, q_in, k_in, v_in, q_buf, out, in_attn: bool) -> None:
-    """The type combinations a streaming step is built for, checked before its first launch:
-    bf16 inputs; a bf16 or E4M3 key cache whose value cache has the same type (or f16 values
-    with bf16 keys); queries buffered in the key cache's type; a bf16 output."""
+def _check_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, angles, rope: bool,
+                in_attn: bool) -> None:
+    """What a streaming step is built for, checked before its first launch. Shapes: the chunk's
+    q_in [B, Lc, Hq, d] and k_in, v_in [B, Lc, Hkv, d] contiguous, with the cache's B, Lc, Hkv
+    and d (a chunk of another length would write past its slot range), Hq a multiple of Hkv,
+    q_buf and out of q_in's shape, angles with the rows the RoPE scope reads. Types: bf16 inputs;
+    a bf16 or E4M3 key cache whose value cache has the same type (or f16 values with bf16 keys);
+    queries buffered in the key cache's type; a bf16 output."""
     fn = "stream_self_attention_step"
+    B, Lc, Hkv, d = cache.B, cache.chunk_len, cache.Hkv, cache.d
+    for name, t in (("k_in", k_in), ("v_in", v_in)):
+        if tuple(t.shape) != (B, Lc, Hkv, d) or not t.is_contiguous():
+            raise StreamAttnError(fn, SA_ERR_SHAPE_CODE,
+                                  f"{name} must be a contiguous [{B}, {Lc}, {Hkv}, {d}] chunk, got {tuple(t.shape)}")
+    if (q_in.dim() != 4 or tuple(q_in.shape[:2]) != (B, Lc) or q_in.shape[3] != d or q_in.shape[2] % Hkv
+            or not q_in.is_contiguous()):
+        raise StreamAttnError(fn, SA_ERR_SHAPE_CODE,
+                              f"q_in must be a contiguous [{B}, {Lc}, Hq, {d}] chunk with Hq a multiple of {Hkv}, "
+                              f"got {tuple(q_in.shape)}")
+    for name, t in (("q_buf", None if in_attn else q_buf), ("out", out)):
+        if t is not None and (tuple(t.shape) != tuple(q_in.shape) or not t.is_contiguous()):
+            raise StreamAttnError(fn, SA_ERR_SHAPE_CODE, f"{name} must be contiguous with q_in's shape {tuple(q_in.shape)}")
+    if rope:
+        # before-cache RoPE reads the chunk's Lc rows; after-cache RoPE one row per visible key
+        rows = kv_cache_slot(chunk_idx, Lc, cache.sink_size, cache.window_size)[1] if cache.k_rot is not None else Lc
+        if (angles is None or angles.dim() != 2 or angles.shape[1] != d // 2 or angles.shape[0] < rows
+                or angles.dtype != torch.float32 or not angles.is_contiguous()):
+            raise StreamAttnError(fn, SA_ERR_SHAPE_CODE, f"angles must be contiguous fp32 [>= {rows}, {d // 2}]")
     _require_bf16(fn, q_in, k_in, v_in)
     kt, vt = cache.k.dtype, cache.v.dtype
     if kt not in (torch.bfloat16, torch.float8_e4m3fn):
@@ -421,13 +462,13 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
     """
     in_attn = (query_in_attention and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
                cache.v.dtype == torch.bfloat16)
-    _check_step_dtypes(cache, q_in, k_in, v_in, q_buf, out, in_attn)
+    rope = rope_style != SA_ROPE_NONE
+    _check_step(cache, chunk_idx, q_in, k_in, v_in, q_buf, out, angles, rope, in_attn)
     slot, visible = cache.before_update(chunk_idx)
     S = cache.capacity
     after = cache.k_rot is not None
     q_angles = angles[visible - cache.chunk_len:visible] if after else angles
     flag = SA_ROPE_AFTER_CACHE if after else 0
-    rope = rope_style != SA_ROPE_NONE
     style = (rope_style | flag) if rope else SA_ROPE_NONE
     bstride = S * cache.Hkv * cache.d
     if in_attn:
@@ -456,3 +497,52 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
         attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
     cache.after_update(chunk_idx)
     return visible
+
+
+def context_kv(k_in, v_in, cache_k, cache_v, gamma_k=None, eps: float = 1e-6, norm_scope: int = SA_NORM_HEAD,
+               angles=None, rope_style: int = SA_ROPE_SPLIT):
+    """Static cross-attention context cache (the compute_kv step): context keys k_in [B, S, H, d]
+    RMS-normalised (no weights: not normalised) into cache_k, and rotated with angles [S, d/2]
+    for before-cache RoPE or left unrotated (angles None) for after-cache RoPE; values copied
+    into cache_v. One prologue launch; bf16 in, the caches' type out."""
+    scope = norm_scope if gamma_k is not None else SA_NORM_NONE
+    style = rope_style if angles is not None else SA_ROPE_NONE
+    qk_norm_rope_v(k_in, cache_k, v_in, cache_v, gamma_k, angles, eps, scope, style)
+
+
+def cross_attention_step(context_k, context_v, q_in, out, gamma_q, eps: float, scale: float, q_buf=None,
+                         q_angles=None, context_angles=None, k_rot=None, rope_style: int = SA_ROPE_SPLIT,
+                         workspace=None):
+    """One query chunk of cross-attention over a static context cache (context_kv), as library calls.
+
+    * No RoPE (q_angles None): the query RMSNorm (head scope, gamma_q) runs inside the attention
+      as it loads each query row (attn_forward_qnorm); q_buf is not used.
+    * Before-cache RoPE (q_angles given, context_angles None): the cached keys were rotated by
+      context_kv; qk_norm_rope normalises and rotates the queries into q_buf, then attention.
+    * After-cache RoPE (q_angles and context_angles given): the cache holds unrotated keys, and
+      every call rotates all S of them with the cache-relative angle rows context_angles[0:S] into
+      k_rot ([B, S, H, d] bf16, not the cache). A static context cache is the rolling cache after
+      its one and only chunk (chunk length = window = S, no sink), whose rows are in logical
+      order, so kv_cache_rope does this. The queries are normalised and rotated with q_angles
+      [Lq, d/2] into q_buf, then attention runs over k_rot.
+    workspace (attn_workspace) lets the attention run balanced when its grid would leave CUs idle."""
+    if q_angles is None:
+        if context_angles is not None:
+            raise StreamAttnError("cross_attention_step", SA_ERR_SHAPE_CODE, "context angles without query angles")
+        return attn_forward_qnorm(q_in, context_k, context_v, out, scale, gamma_q, eps, workspace=workspace)
+    if q_buf is None or q_buf.shape != q_in.shape or q_buf.dtype != torch.bfloat16:
+        raise StreamAttnError("cross_attention_step", SA_ERR_SHAPE_CODE, "q_buf must be a bf16 tensor of q_in's shape")
+    B, S, Hkv, d = context_k.shape
+    keys = context_k
+    if context_angles is not None:
+        if k_rot is None or k_rot.shape != context_k.shape or k_rot.data_ptr() == context_k.data_ptr():
+            raise StreamAttnError("cross_attention_step", SA_ERR_SHAPE_CODE, "k_rot must be a separate buffer of the cache's shape")
+        if context_angles.shape[0] < S:
+            raise StreamAttnError("cross_attention_step", SA_ERR_SHAPE_CODE, f"context angles need {S} rows")
+        kv_cache_rope(context_k, k_rot, context_angles, 0, S, 0, S, rope_style)
+        keys = k_rot
+    qk_norm_rope(q_in, q_buf, None, None, gamma_q, None, q_angles, eps,
+                 SA_NORM_HEAD if gamma_q is not None else SA_NORM_NONE, rope_style, Hkv=0)
+    if workspace is not None:
+        return attn_forward_ws(q_buf, keys, context_v, out, scale, workspace)
+    return attn_forward_kvstride(q_buf, keys, context_v, out, S, scale, False)

@@ -111,6 +111,10 @@ WORKLOADS = {
     # cross-attention over a static 512-token context, B = 2 (guidance pair), Q RMSNorm only
     "cross_1785x512": Workload("cross_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
                                128 ** -0.5, 1004, "q_norm"),
+    # the same cross-attention with after-cache RoPE: the static context cache keeps unrotated keys,
+    # each query chunk rotates all 512 of them (cache-relative rows) and its queries (rows after them)
+    "cross_after_1785x512": Workload("cross_after_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
+                                     128 ** -0.5, 1004, "q_norm", rope_scope="after"),
     # the cross-attention context cache with V kept in f16 (bit-identical outputs)
     "cross_vf16_1785x512": Workload("cross_vf16_1785x512", 2, 40, 40, 1785, 512, 128, "bf16", False,
                                     128 ** -0.5, 1004, "q_norm", v_cache_dtype="f16"),

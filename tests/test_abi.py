@@ -355,3 +355,74 @@ def test_binding_streaming_step_rejects_unbuilt_dtype_combinations(kdt, vdt, qdt
         binding.stream_self_attention_step(cache, 0, x, x, x, q_buf, out, g, g, ang, 1e-6, 0.125)
     assert e.value.status == code
     assert rec.calls == [] and cache._current is None  # nothing launched, no chunk opened
+
+
+def _step_args(B=1, Lc=4, H=2, d=64, **over):
+    import torch
+    a = dict(q_in=torch.zeros((B, Lc, H, d), dtype=torch.bfloat16), k_in=torch.zeros((B, Lc, H, d), dtype=torch.bfloat16),
+             v_in=torch.zeros((B, Lc, H, d), dtype=torch.bfloat16), q_buf=torch.zeros((B, Lc, H, d), dtype=torch.bfloat16),
+             out=torch.zeros((B, Lc, H, d), dtype=torch.bfloat16), gamma_q=torch.ones(d), gamma_k=torch.ones(d),
+             angles=torch.zeros((Lc, d // 2)))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("what", ["short_chunk", "long_chunk", "kv_heads", "head_dim", "q_heads_not_multiple",
+                                  "noncontiguous_k", "out_shape", "angles_rows", "angles_dtype", "batch"])
+def test_binding_streaming_step_rejects_shape_changes(what, monkeypatch):
+    """A chunk whose shape differs from the cache's (length, heads, head dim, batch), or angles
+    with too few rows, is rejected before any launch: a longer chunk would otherwise be written
+    past its slot range into the next chunk's rows or past the cache."""
+    import torch
+    from head_attention_streaming_amd import binding
+    rec = _RecordingLib()
+    monkeypatch.setattr(binding, "lib", lambda: rec)
+    B, Lc, H, d = 1, 4, 2, 64
+    cache = binding.BlockKVCache(B, H, d, Lc, 0, 2 * Lc, device="cpu")
+    bf = dict(dtype=torch.bfloat16)
+    bad = {
+        "short_chunk": dict(k_in=torch.zeros((B, Lc - 1, H, d), **bf)),
+        "long_chunk": dict(q_in=torch.zeros((B, Lc + 1, H, d), **bf), k_in=torch.zeros((B, Lc + 1, H, d), **bf),
+                           v_in=torch.zeros((B, Lc + 1, H, d), **bf), q_buf=torch.zeros((B, Lc + 1, H, d), **bf),
+                           out=torch.zeros((B, Lc + 1, H, d), **bf), angles=torch.zeros((Lc + 1, d // 2))),
+        "kv_heads": dict(v_in=torch.zeros((B, Lc, H + 1, d), **bf)),
+        "head_dim": dict(q_in=torch.zeros((B, Lc, H, 128), **bf)),
+        "q_heads_not_multiple": dict(q_in=torch.zeros((B, Lc, 3, d), **bf), q_buf=torch.zeros((B, Lc, 3, d), **bf),
+                                     out=torch.zeros((B, Lc, 3, d), **bf)),
+        "noncontiguous_k": dict(k_in=torch.zeros((B, H, Lc, d), **bf).transpose(1, 2)),
+        "out_shape": dict(out=torch.zeros((B, Lc, H + 2, d), **bf)),
+        "angles_rows": dict(angles=torch.zeros((Lc - 1, d // 2))),
+        "angles_dtype": dict(angles=torch.zeros((Lc, d // 2), dtype=torch.float64)),
+        "batch": dict(q_in=torch.zeros((2, Lc, H, d), **bf), k_in=torch.zeros((2, Lc, H, d), **bf),
+                      v_in=torch.zeros((2, Lc, H, d), **bf), q_buf=torch.zeros((2, Lc, H, d), **bf),
+                      out=torch.zeros((2, Lc, H, d), **bf)),
+    }[what]
+    a = _step_args(B, Lc, H, d, **bad)
+    with pytest.raises(binding.StreamAttnError) as e:
+        binding.stream_self_attention_step(cache, 0, a["q_in"], a["k_in"], a["v_in"], a["q_buf"], a["out"],
+                                           a["gamma_q"], a["gamma_k"], a["angles"], 1e-6, 0.125)
+    assert e.value.status == binding.SA_ERR_SHAPE_CODE
+    assert rec.calls == [] and cache._current is None
+
+
+def test_block_kv_cache_lifecycle_order_and_reset():
+    """Chunks of a stream are written in order; chunk 0 (or reset()) restarts the stream; a
+    skipped or repeated chunk is rejected (it would expose rows another stream wrote)."""
+    from head_attention_streaming_amd import binding
+    cache = binding.BlockKVCache(1, 2, 64, 4, 4, 8, device="cpu")
+    for c in range(5):
+        assert cache.before_update(c) == binding.kv_cache_slot(c, 4, 4, 8)
+        cache.after_update(c)
+    for bad in (4, 6, 3):
+        with pytest.raises(binding.StreamAttnError):
+            cache.before_update(bad)
+    assert cache.before_update(0) == (0, 4)   # a restart sees only its own first chunk
+    cache.after_update(0)
+    assert cache.before_update(1) == (4, 8)
+    with pytest.raises(RuntimeError):
+        cache.reset()                          # not between before_update and after_update
+    cache.after_update(1)
+    cache.reset()
+    with pytest.raises(binding.StreamAttnError):
+        cache.before_update(2)
+    assert cache.before_update(0) == (0, 4)

@@ -601,3 +601,118 @@ def test_streaming_without_norm_or_rope(v_dtype):
         s0 = model.slot_of(c)
         assert np.array_equal(widen(cache.k[:, s0:s0 + Lc]).reshape(k.shape), keys[c])
         assert np.array_equal(widen(q_buf).reshape(q.shape), widen(q).reshape(q.shape))
+
+
+@pytest.mark.parametrize("B,Lq,S,H,d,style,mode,rows_n", [
+    (2, 300, 130, 4, 128, binding.SA_ROPE_SPLIT, "after", None),
+    (1, 97, 65, 3, 64, binding.SA_ROPE_INTERLEAVED, "after", None),
+    (2, 130, 200, 2, 128, binding.SA_ROPE_SPLIT, "before", None),
+    (2, 200, 64, 4, 64, binding.SA_ROPE_NONE, "none", None),
+    (2, 1785, 512, 40, 128, binding.SA_ROPE_SPLIT, "after", 4096),   # the cross-attention workload's shape
+], ids=["after_split_d128", "after_interleaved_d64", "before_split_d128", "norm_only_d64", "after_full_size"])
+def test_cross_attention_context_cache_rope_scopes(B, Lq, S, H, d, style, mode, rows_n):
+    """Cross-attention over a static context cache built once by context_kv (keys RMS-normalised;
+    rotated there for before-cache RoPE, left unrotated for after-cache RoPE), then one query
+    chunk through cross_attention_step, called twice (the cache is reused and stays unrotated).
+    After-cache RoPE rotates all S cached keys with the cache-relative rows 0 .. S-1 of the
+    context angle table and the queries with their own rows (here positions S + i, right after
+    the context). Oracle: RMSNorm, RoPE in fp64, each rounded once to the bf16 that is stored or
+    attended; every row (sampled rows at full size)."""
+    print(f"[case] B={B} Lq={Lq} S={S} H={H} d={d} style={style} mode={mode}", flush=True)
+    eps, scale = 1e-6, d ** -0.5
+    g = torch.Generator().manual_seed(8100 + S + d)
+    q = synthetic.normal((B, Lq, H, d), "bf16", g)
+    k = synthetic.normal((B, S, H, d), "bf16", g)
+    v = synthetic.normal((B, S, H, d), "bf16", g)
+    gq, gk = synthetic.norm_weight(d, g), synthetic.norm_weight(d, g)
+    ctx_ang = synthetic.rope_angles(np.arange(S), d)
+    q_ang = synthetic.rope_angles(np.arange(S, S + Lq), d)
+    ck = torch.full((B, S, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    cv = torch.full_like(ck, float("nan"))
+    binding.context_kv(k.to(DEV), v.to(DEV), ck, cv, gk.to(DEV), eps,
+                       angles=ctx_ang.to(DEV) if mode == "before" else None, rope_style=style)
+    ck_before = ck.clone()
+    k_rot = torch.empty_like(ck) if mode == "after" else None
+    q_buf = torch.empty((B, Lq, H, d), dtype=torch.bfloat16, device=DEV)
+    outs = []
+    for _ in range(2):
+        out = torch.full((B, Lq, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        binding.cross_attention_step(ck, cv, q.to(DEV), out, gq.to(DEV), eps, scale, q_buf=q_buf,
+                                     q_angles=q_ang.to(DEV) if mode != "none" else None,
+                                     context_angles=ctx_ang.to(DEV) if mode == "after" else None, k_rot=k_rot,
+                                     rope_style=style)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(ck.view(torch.int16), ck_before.view(torch.int16))   # the cache is never rotated in place
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    # the context cache: normalised keys (rotated for before-cache RoPE), values bit for bit
+    kcache_ref = _oracle_prologue(k, gk, eps, ctx_ang if mode == "before" else None, style)
+    assert_within_one_ulp(ck, kcache_ref, "context keys")
+    assert np.array_equal(widen(cv).reshape(v.shape), widen(v).reshape(v.shape))
+    K = widen(ck).reshape(k.shape)   # what the cache holds
+    if mode == "after":
+        rot = oracle.rope(K, ctx_ang.double().numpy(), style)
+        assert_within_one_ulp(k_rot, rot, "rotated keys")
+        K = oracle.round_to(rot, "bf16")
+    Q = oracle.round_to(_oracle_prologue(q, gq, eps, q_ang if mode != "none" else None, style), "bf16")
+    V = widen(v).reshape(v.shape)
+    if rows_n is None:
+        assert_attention_close(outs[0], oracle.attention(Q, K, V, scale), mode)
+    else:
+        rows = sample_rows(B, Lq, H, rows_n, seed=5)
+        ref = oracle.attention(Q, K, V, scale, rows=rows)
+        assert_attention_close(outs[0].reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, mode)
+
+
+@pytest.mark.parametrize("after", [False, True], ids=["before_cache_rope", "after_cache_rope"])
+def test_cache_reset_matches_fresh_cache(after):
+    """A cache used by one stream (fill and eviction), then restarted at chunk 0 by a second
+    stream, gives that stream the outputs of a fresh cache bit for bit (stale rows of the first
+    stream are never visible), and matches the oracle's rolling-cache model of the second stream."""
+    B, Lc, H, d, sink, window = 1, 64, 4, 128, 64, 128
+    eps, scale = 1e-6, d ** -0.5
+    print(f"[case] reset after={after}", flush=True)
+    used = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after)
+    fresh = binding.BlockKVCache(B, H, d, Lc, sink, window, device=DEV, after_cache_rope=after)
+    g = torch.Generator().manual_seed(9100)
+    gq, gk = synthetic.norm_weight(d, g).to(DEV), synthetic.norm_weight(d, g).to(DEV)
+
+    def chunk(seed, c):
+        gc = torch.Generator().manual_seed(seed + c)
+        return [synthetic.normal((B, Lc, H, d), "bf16", gc) for _ in range(3)]
+
+    def angles(c):
+        n = min((c + 1) * Lc, sink + window)
+        return synthetic.rope_angles(np.arange(n) if after else np.arange(c * Lc, (c + 1) * Lc), d)
+
+    def run(cache, seed, c):
+        q, k, v = chunk(seed, c)
+        q_buf = torch.empty((B, Lc, H, d), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty_like(q_buf)
+        binding.stream_self_attention_step(cache, c, q.to(DEV), k.to(DEV), v.to(DEV), q_buf, out, gq, gk,
+                                           angles(c).to(DEV), eps, scale)
+        return out
+
+    for c in range(5):              # first stream: fill, then two evictions
+        run(used, 500, c)
+    used.reset()
+    model = RollingCacheModel(Lc, sink, window)
+    kstar, vals = {}, {}
+    for c in range(4):              # second stream on both caches
+        o_used, o_fresh = run(used, 700, c), run(fresh, 700, c)
+        torch.cuda.synchronize()
+        assert torch.equal(o_used.view(torch.int16), o_fresh.view(torch.int16)), c
+        q, k, v = chunk(700, c)
+        model.write(c)
+        n = model.visible_len()
+        ang = angles(c)
+        ang_q = ang[n - Lc:] if after else ang
+        qs = oracle.round_to(_oracle_prologue(q, gq.cpu(), eps, ang_q, binding.SA_ROPE_SPLIT), "bf16")
+        kstar[c] = oracle.round_to(_oracle_prologue(k, gk.cpu(), eps, None if after else ang, binding.SA_ROPE_SPLIT),
+                                   "bf16")
+        vals[c] = widen(v).reshape(v.shape)
+        K = np.concatenate([kstar[x] for x in model.visible_chunks()], axis=1)
+        if after:
+            K = oracle.round_to(oracle.rope(K, ang.double().numpy(), binding.SA_ROPE_SPLIT), "bf16")
+        V = np.concatenate([vals[x] for x in model.visible_chunks()], axis=1)
+        assert_attention_close(o_used, oracle.attention(qs, K, V, scale), f"restarted chunk {c}")
