@@ -311,6 +311,85 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             }
         }
     }
+    // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, EPC input
+    // features from scol) of every tile; rows past Lk re-read row Lk - 1 (their scores are
+    // masked). When a tile has fewer chunks than the group has threads, whole waves sit out.
+    const int tid_g = KS == 1 ? tid : tid % kGThreads;
+    const bool stager = kChunks >= kGThreads || tid_g < kChunks;
+    const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * EPC;
+    // K and V rows of this (batch, K/V head) are read through buffer resources that end at row
+    // Lk: rows at or past Lk fall outside the range and read as zero (their scores are masked).
+    // A thread's byte offset is a constant plus the tile's first row; when the rows up to one
+    // tile past Lk span 4 GiB or more (BIG), each tile gets a resource rebased at its first row
+    // instead, so every offset stays within 32 bits.
+    const char* const kbase = reinterpret_cast<const char*>(pk + b * p.kv_bstride + hk * D);
+    const char* const vbase = reinterpret_cast<const char*>(pv + b * p.kv_bstride + hk * D);
+    const uint32_t row_bytes = (uint32_t)p.kv_tstride * (uint32_t)sizeof(In);
+    const uint32_t tile_bytes = (uint32_t)kBN * row_bytes;
+    const uint32_t voff0 = (uint32_t)srow0 * row_bytes + (uint32_t)(scol * sizeof(In));
+    const uint32_t region_bytes = BIG ? 0u : (uint32_t)p.Lk * row_bytes;
+    const auto k_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)region_bytes, kBufferWord3);
+    const auto v_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)region_bytes, kBufferWord3);
+    auto tile_rsrc = [&](const char* base, int kt) __attribute__((always_inline)) {
+        const int64_t row0 = (int64_t)kt * kBN;
+        const int64_t bytes = min64(max64(0, p.Lk - row0) * row_bytes, 0xffffffffLL);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + row0 * row_bytes), (short)0,
+                                                  (int)(uint32_t)bytes, kBufferWord3);
+    };
+    In* const Kg = &Ks[ks][0];  // this group's K and V slots (V always f16 in LDS)
+    uint16_t* const Vg = &Vs[ks][0];
+    In* ks_st = Kg + srow0 * KST + scol;
+    uint16_t* vs_st = Vg + srow0 * VST + scol;
+    u32x4 kreg[NCH], vreg[NCH];
+    auto load_rows = [&](u32x4 (&dst)[NCH], const char* base, const __amdgpu_buffer_rsrc_t& whole, int kt)
+                         __attribute__((always_inline)) {
+        if (!stager) return;
+        if constexpr (!BIG) {
+            const uint32_t toff = (uint32_t)kt * tile_bytes;
+            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(whole, voff0 + (toff + (uint32_t)(u * RSTEP) * row_bytes), 0, 0);
+            });
+        } else {
+            const auto r = tile_rsrc(base, kt);
+            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff0 + (uint32_t)(u * RSTEP) * row_bytes, 0, 0);
+            });
+        }
+    };
+    auto load_k = [&](int kt) __attribute__((always_inline)) { load_rows(kreg, kbase, k_rsrc, kt); };
+    auto load_v = [&](int kt) __attribute__((always_inline)) { load_rows(vreg, vbase, v_rsrc, kt); };
+    auto store_k = [&](int slot) __attribute__((always_inline)) {
+        if (!stager) return;
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x4*>(ks_st + slot * (kBN * KST) + u * RSTEP * KST) = kreg[u];
+        });
+    };
+    auto store_v = [&](int slot) __attribute__((always_inline)) {
+        if (!stager) return;
+        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
+            uint16_t* dst = vs_st + slot * (kBN * VST) + u * RSTEP * VST;
+            if constexpr (FP8) {
+                u32x4 lo, hi;
+                fp8x16_to_f16x16(vreg[u], lo, hi);
+                *reinterpret_cast<u32x4*>(dst) = lo;
+                *reinterpret_cast<u32x4*>(dst + 8) = hi;
+            } else {
+                *reinterpret_cast<u32x4*>(dst) = V_BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
+            }
+        });
+    };
+
+    // The first tiles' loads go out right behind the query loads -- K(ta), V(ta) and K(ta + 1),
+    // the last into registers of its own -- so for short key loops their latency overlaps the
+    // queries' and the query norm's instead of following them (V(ta) and K(ta + 1) used to wait
+    // for K(ta) to reach LDS). Balanced launches (key loops of 32+ tiles, at their register
+    // limit) load K(ta + 1) after K(ta) is staged, as before.
+    u32x4 knext[NCH];
+    if (nkt > t0) {
+        load_k(ta);
+        load_v(ta);
+        if constexpr (!SK) load_rows(knext, kbase, k_rsrc, min(ta + 1, nkt - 1));
+    }
     if constexpr (!FP8) {
         if (p.gamma_q) {  // uniform. RMSNorm of the query row, then one rounding to the input type:
             // gamma * (z * r), r = 1 / sqrt(mean(z^2) + eps); this lane holds half of the row's
@@ -384,74 +463,6 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             }
         }
     }
-
-    // Staging geometry: thread tid copies 16-byte chunks (key row srow0 + u*RSTEP, EPC input
-    // features from scol) of every tile; rows past Lk re-read row Lk - 1 (their scores are
-    // masked). When a tile has fewer chunks than the group has threads, whole waves sit out.
-    const int tid_g = KS == 1 ? tid : tid % kGThreads;
-    const bool stager = kChunks >= kGThreads || tid_g < kChunks;
-    const int srow0 = tid_g / CPR, scol = (tid_g % CPR) * EPC;
-    // K and V rows of this (batch, K/V head) are read through buffer resources that end at row
-    // Lk: rows at or past Lk fall outside the range and read as zero (their scores are masked).
-    // A thread's byte offset is a constant plus the tile's first row; when the rows up to one
-    // tile past Lk span 4 GiB or more (BIG), each tile gets a resource rebased at its first row
-    // instead, so every offset stays within 32 bits.
-    const char* const kbase = reinterpret_cast<const char*>(pk + b * p.kv_bstride + hk * D);
-    const char* const vbase = reinterpret_cast<const char*>(pv + b * p.kv_bstride + hk * D);
-    const uint32_t row_bytes = (uint32_t)p.kv_tstride * (uint32_t)sizeof(In);
-    const uint32_t tile_bytes = (uint32_t)kBN * row_bytes;
-    const uint32_t voff0 = (uint32_t)srow0 * row_bytes + (uint32_t)(scol * sizeof(In));
-    const uint32_t region_bytes = BIG ? 0u : (uint32_t)p.Lk * row_bytes;
-    const auto k_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)region_bytes, kBufferWord3);
-    const auto v_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)region_bytes, kBufferWord3);
-    auto tile_rsrc = [&](const char* base, int kt) __attribute__((always_inline)) {
-        const int64_t row0 = (int64_t)kt * kBN;
-        const int64_t bytes = min64(max64(0, p.Lk - row0) * row_bytes, 0xffffffffLL);
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + row0 * row_bytes), (short)0,
-                                                  (int)(uint32_t)bytes, kBufferWord3);
-    };
-    In* const Kg = &Ks[ks][0];  // this group's K and V slots (V always f16 in LDS)
-    uint16_t* const Vg = &Vs[ks][0];
-    In* ks_st = Kg + srow0 * KST + scol;
-    uint16_t* vs_st = Vg + srow0 * VST + scol;
-    u32x4 kreg[NCH], vreg[NCH];
-    auto load_rows = [&](u32x4 (&dst)[NCH], const char* base, const __amdgpu_buffer_rsrc_t& whole, int kt)
-                         __attribute__((always_inline)) {
-        if (!stager) return;
-        if constexpr (!BIG) {
-            const uint32_t toff = (uint32_t)kt * tile_bytes;
-            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(whole, voff0 + (toff + (uint32_t)(u * RSTEP) * row_bytes), 0, 0);
-            });
-        } else {
-            const auto r = tile_rsrc(base, kt);
-            static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff0 + (uint32_t)(u * RSTEP) * row_bytes, 0, 0);
-            });
-        }
-    };
-    auto load_k = [&](int kt) __attribute__((always_inline)) { load_rows(kreg, kbase, k_rsrc, kt); };
-    auto load_v = [&](int kt) __attribute__((always_inline)) { load_rows(vreg, vbase, v_rsrc, kt); };
-    auto store_k = [&](int slot) __attribute__((always_inline)) {
-        if (!stager) return;
-        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            *reinterpret_cast<u32x4*>(ks_st + slot * (kBN * KST) + u * RSTEP * KST) = kreg[u];
-        });
-    };
-    auto store_v = [&](int slot) __attribute__((always_inline)) {
-        if (!stager) return;
-        static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            uint16_t* dst = vs_st + slot * (kBN * VST) + u * RSTEP * VST;
-            if constexpr (FP8) {
-                u32x4 lo, hi;
-                fp8x16_to_f16x16(vreg[u], lo, hi);
-                *reinterpret_cast<u32x4*>(dst) = lo;
-                *reinterpret_cast<u32x4*>(dst + 8) = hi;
-            } else {
-                *reinterpret_cast<u32x4*>(dst) = V_BF16 ? bf16x8_to_f16x8(vreg[u]) : vreg[u];
-            }
-        });
-    };
 
     // LDS read addresses (address space 3, so constant offsets fold into the instructions).
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
@@ -630,10 +641,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     };
 
     if (nkt > t0) {  // uniform over the workgroup: every group runs nsteps + 1 steps
-        load_k(ta);
         store_k(ta & 1);
-        load_k(min(ta + 1, nkt - 1));
-        load_v(ta);
+        if constexpr (SK)
+            load_k(min(ta + 1, nkt - 1));
+        else
+            static_for<NCH>([&](auto u) __attribute__((always_inline)) { kreg[u] = knext[u]; });
         __syncthreads();
         const bool mask0 = ta < tl || ta >= tr;
         if (ta & 1) {
