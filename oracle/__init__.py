@@ -72,7 +72,8 @@ def _load():
         lib.oracle_rope.argtypes = [P, P, P, I, I, I, I, I]
         lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I]
         lib.oracle_attention.restype = I
-        lib.oracle_attention_spread.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I, P, P, P]
+        lib.oracle_attention_spread.argtypes = [P, P, P, P, P, I64, I, I, I, I, I, I, D, I64, I64, I, P, P, P, D, P,
+                                                P]
         lib.oracle_attention_spread.restype = I
         _lib = lib
     return _lib
@@ -230,12 +231,14 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
 
 def attention_spread(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
                      rows: np.ndarray | None = None, nthreads: int | None = None,
-                     window: tuple[int, int] | None = None):
+                     window: tuple[int, int] | None = None, tail_binades: float = np.inf):
     """``attention`` plus what a tolerance for rounded softmax weights needs, from the exact
     weights w_j = softmax(s)_j of each row: A = sum_j w_j |v_j - o| and R = sqrt(sum_j w_j^2
-    (v_j - o)^2) per output element (same shape as the output), and the row's score range
-    max_j s_j - min_j s_j in base-2 exponent units (shape: the output without its last axis).
-    Returns (o, A, R, span)."""
+    (v_j - o)^2) per output element (same shape as the output), the row's score range
+    max_j s_j - min_j s_j in base-2 exponent units (shape: the output without its last axis), and
+    for the keys whose score lies more than tail_binades (base-2 units) below the row maximum,
+    their part of A (A_tail, the output's shape) and their total weight (W_tail, a row's shape).
+    Returns (o, A, R, span, A_tail, W_tail)."""
     if window is not None and causal:
         raise ValueError("give either causal or window")
     win_left, win_right = window if window is not None else ((-1, 0) if causal else (-1, -1))
@@ -250,13 +253,17 @@ def attention_spread(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
     a = np.empty((nrows, d))
     r = np.empty((nrows, d))
     span = np.empty((nrows,))
+    ta = np.empty((nrows, d))
+    tw = np.empty((nrows,))
     rc = _load().oracle_attention_spread(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                          None if rows_arr is None else _ptr(rows_arr), nrows, B, Hq, k.shape[2],
                                          Lq, k.shape[1], d, float(scale), int(win_left), int(win_right),
-                                         nthreads or default_threads(), _ptr(a), _ptr(r), _ptr(span))
+                                         nthreads or default_threads(), _ptr(a), _ptr(r), _ptr(span),
+                                         float(tail_binades), _ptr(ta), _ptr(tw))
     if rc != 0:
         raise RuntimeError("oracle_attention_spread failed")
     if rows is None:
-        return (out.reshape(B, Lq, Hq, d), a.reshape(B, Lq, Hq, d), r.reshape(B, Lq, Hq, d),
-                span.reshape(B, Lq, Hq))
-    return out, a, r, span
+        sh = (B, Lq, Hq)
+        return (out.reshape(*sh, d), a.reshape(*sh, d), r.reshape(*sh, d), span.reshape(sh), ta.reshape(*sh, d),
+                tw.reshape(sh))
+    return out, a, r, span, ta, tw

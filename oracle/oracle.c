@@ -138,6 +138,10 @@ typedef struct {
      * sqrt(sum_j w_j^2 (v_jt - o_t)^2) with w_j = p_j / l the exact weights; span[n] = the range
      * of the row's visible scores, max_j s_j - min_j s_j, in base-2 exponent units (times log2 e) */
     double *spread_a, *spread_r, *span;
+    /* keys whose score lies more than tail_binades (base-2 units) below the row maximum: their
+     * part of spread_a (tail_a[n*d + t]) and their total weight (tail_w[n]) */
+    double tail_binades;
+    double *tail_a, *tail_w;
 } attn_job;
 
 /* One query row: s_j = scale * <q_i, k_j> for every visible key j, then
@@ -181,21 +185,28 @@ static void attention_row(const attn_job* J, int64_t row, double* scores, double
         const int64_t n_out = o - J->out;   /* this row's offset into the outputs */
         double* a = J->spread_a + n_out;
         double* r = J->spread_r + n_out;
-        for (int t = 0; t < d; ++t) a[t] = r[t] = 0.0;
+        double* ta = J->tail_a + n_out;
+        double tw = 0.0;
+        for (int t = 0; t < d; ++t) a[t] = r[t] = ta[t] = 0.0;
         double smin = INFINITY;
         for (int64_t n = 0; n < nvis; ++n) {
             const double w = scores[n] / l;
             const double* vj = J->v + (((int64_t)b * J->Lk + jlo + n) * J->Hkv + hk) * d;
+            /* scores[n] = exp(s_n - m): below 2^-tail_binades lies in the tail */
+            const int tail = -log2(scores[n]) > J->tail_binades;
+            if (tail) tw += w;
             for (int t = 0; t < d; ++t) {
                 const double dev = vj[t] - o[t];
                 a[t] += w * fabs(dev);
                 r[t] += (w * dev) * (w * dev);
+                if (tail) ta[t] += w * fabs(dev);
             }
             /* scores[n] holds exp(s_n - m): the smallest gives the row's score range */
             if (scores[n] < smin) smin = scores[n];
         }
         for (int t = 0; t < d; ++t) r[t] = sqrt(r[t]);
         J->span[n_out / d] = nvis > 0 ? -log2(smin) : 0.0;
+        J->tail_w[n_out / d] = tw;
     }
 }
 
@@ -219,31 +230,32 @@ static void* attention_worker(void* arg) {
 static int run_attention(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
                          int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
                          int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
-                         double* span);
+                         double* span, double tail_binades, double* tail_a, double* tail_w);
 
 int oracle_attention(const double* q, const double* k, const double* v, double* out,
                      const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
                      double scale, int64_t win_left, int64_t win_right, int nthreads) {
     return run_attention(q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, nthreads,
-                         NULL, NULL, NULL);
+                         NULL, NULL, NULL, 0.0, NULL, NULL);
 }
 
 /* oracle_attention plus, per output element, the spread of V under the exact softmax weights
- * (spread_a, spread_r: [nrows, d]) and, per row, the range of its scores in base-2 units (span:
- * [nrows]); see attn_job. Same return values. */
+ * (spread_a, spread_r: [nrows, d]), per row the range of its scores in base-2 units (span:
+ * [nrows]), and the part of spread_a and of the weight that keys more than tail_binades below
+ * the row maximum carry (tail_a: [nrows, d], tail_w: [nrows]); see attn_job. Same return values. */
 int oracle_attention_spread(const double* q, const double* k, const double* v, double* out,
                             const int64_t* rows, int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d,
                             double scale, int64_t win_left, int64_t win_right, int nthreads, double* spread_a,
-                            double* spread_r, double* span) {
-    if (!spread_a || !spread_r || !span) return -1;
+                            double* spread_r, double* span, double tail_binades, double* tail_a, double* tail_w) {
+    if (!spread_a || !spread_r || !span || !tail_a || !tail_w) return -1;
     return run_attention(q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, scale, win_left, win_right, nthreads,
-                         spread_a, spread_r, span);
+                         spread_a, spread_r, span, tail_binades, tail_a, tail_w);
 }
 
 static int run_attention(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
                          int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
                          int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
-                         double* span) {
+                         double* span, double tail_binades, double* tail_a, double* tail_w) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Lq < 0 || Lk < 0 || d <= 0) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -253,7 +265,7 @@ static int run_attention(const double* q, const double* k, const double* v, doub
     int rc = 0;
     for (int t = 0; t < nthreads; ++t) {
         attn_job J = {q, k, v, out, rows, nrows, B, Hq, Hkv, Lq, Lk, d, win_left, win_right, scale, t, nthreads,
-                      spread_a, spread_r, span};
+                      spread_a, spread_r, span, tail_binades, tail_a, tail_w};
         jobs[t] = J;
         created[t] = 0;
     }

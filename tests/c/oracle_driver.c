@@ -19,7 +19,7 @@ int oracle_attention(const double* q, const double* k, const double* v, double* 
 int oracle_attention_spread(const double* q, const double* k, const double* v, double* out, const int64_t* rows,
                             int64_t nrows, int B, int Hq, int Hkv, int Lq, int Lk, int d, double scale,
                             int64_t win_left, int64_t win_right, int nthreads, double* spread_a, double* spread_r,
-                            double* span);
+                            double* span, double tail_binades, double* tail_a, double* tail_w);
 
 static int fails = 0;
 #define CHECK(c)                                                             \
@@ -129,13 +129,17 @@ int main(void) {
     CHECK(oracle_attention(q, k, v, out, NULL, 0, AB, 3, 2, LQ, LK, AD, 0.25, -1, -1, 1) == -1);
     /* spreads over a row subset, threaded: a single visible key (window (0, 0)) has none */
     double *sa = malloc(sizeof(double) * 3 * AD), *sr = malloc(sizeof(double) * 3 * AD), span[3];
-    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, 0, 0, 2, sa, sr, span) == 0);
-    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] == 0.0 && sr[i] == 0.0);
-    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, -1, -1, 3, sa, sr, span) == 0);
-    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] > 0.0 && sr[i] > 0.0 && sr[i] <= sa[i]);
-    for (int i = 0; i < 3; ++i) CHECK(span[i] > 0.0);
+    double *ta = malloc(sizeof(double) * 3 * AD), tw[3];
+    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, 0, 0, 2, sa, sr, span, 0.5, ta,
+                                  tw) == 0);
+    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] == 0.0 && sr[i] == 0.0 && ta[i] == 0.0);
+    CHECK(oracle_attention_spread(q, k, v, sub, rows, 3, AB, HQ, HKV, LQ, LK, AD, 0.25, -1, -1, 3, sa, sr, span, 1e-3,
+                                  ta, tw) == 0);
+    for (int i = 0; i < 3 * AD; ++i) CHECK(sa[i] > 0.0 && sr[i] > 0.0 && sr[i] <= sa[i] && ta[i] <= sa[i]);
+    for (int i = 0; i < 3; ++i) CHECK(span[i] > 0.0 && tw[i] > 0.0 && tw[i] < 1.0);
     free(sa);
     free(sr);
+    free(ta);
     free(q);
     free(k);
     free(v);

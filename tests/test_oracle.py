@@ -507,9 +507,9 @@ def test_ulp_equals_gap_to_next_bit_pattern(dtype, tdt, idt, lo, hi):
 def test_attention_spread_single_key_is_zero():
     """One visible key: weight 1, o = v, so both spreads and the score range are exactly 0."""
     q, k, v = _rand(1, 3, 2, 8), _rand(1, 1, 2, 8), _rand(1, 1, 2, 8)
-    o, a, r, span = oracle.attention_spread(q, k, v, 0.3)
+    o, a, r, span, ta, tw = oracle.attention_spread(q, k, v, 0.3)
     assert np.array_equal(o, np.broadcast_to(v, o.shape))
-    assert not a.any() and not r.any() and not span.any()
+    assert not a.any() and not r.any() and not span.any() and not ta.any() and not tw.any()
 
 
 def test_attention_spread_uniform_weights_closed_form():
@@ -517,7 +517,7 @@ def test_attention_spread_uniform_weights_closed_form():
     computed here from V alone; the score range is 0."""
     B, Lq, Lk, H, d = 2, 3, 37, 2, 16
     q, k, v = np.zeros((B, Lq, H, d)), _rand(B, Lk, H, d), _rand(B, Lk, H, d)
-    o, a, r, span = oracle.attention_spread(q, k, v, 0.7)
+    o, a, r, span, _, _ = oracle.attention_spread(q, k, v, 0.7)
     mean = v.mean(axis=1, keepdims=True)                       # [B, 1, H, d]
     np.testing.assert_allclose(o, np.broadcast_to(mean, o.shape), rtol=0, atol=1e-14)
     np.testing.assert_allclose(a, np.broadcast_to(np.abs(v - mean).mean(axis=1, keepdims=True), a.shape),
@@ -534,8 +534,14 @@ def test_attention_spread_two_keys_hand_worked():
     q = np.array([[[[math.log(3.0), 0.0]]]])
     k = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])
     v = np.array([[[[4.0, 8.0]], [[0.0, -4.0]]]])
-    o, a, r, span = oracle.attention_spread(q, k, v, 1.0)
+    o, a, r, span, ta, tw = oracle.attention_spread(q, k, v, 1.0, tail_binades=1.5)
     dv = np.array([4.0, 12.0])
+    # key 1 lies log2(3) ~ 1.58 binades below key 0: with a 1.5-binade threshold it is the tail,
+    # carrying weight 1/4 and w1 |v1 - o| = w1 w0 |v0 - v1| of A
+    np.testing.assert_allclose(tw[0, 0, 0], 0.25, rtol=1e-14)
+    np.testing.assert_allclose(ta[0, 0, 0], 3.0 / 16.0 * dv, rtol=1e-13)
+    _, _, _, _, ta2, tw2 = oracle.attention_spread(q, k, v, 1.0, tail_binades=1.6)
+    assert not ta2.any() and not tw2.any()
     np.testing.assert_allclose(o[0, 0, 0], [3.0, 5.0], rtol=1e-14)
     np.testing.assert_allclose(a[0, 0, 0], 3.0 / 8.0 * dv, rtol=1e-13)
     np.testing.assert_allclose(r[0, 0, 0], 3.0 * math.sqrt(2.0) / 16.0 * dv, rtol=1e-13)
@@ -546,10 +552,13 @@ def test_attention_spread_rows_and_windows_match_full():
     """Row subsets and windowed rows give the same o as ``attention`` and the same spreads as the
     full computation."""
     q, k, v = _rand(2, 9, 4, 8), _rand(2, 13, 2, 8), _rand(2, 13, 2, 8)
-    o, a, r, span = oracle.attention_spread(q, k, v, 0.5, window=(3, 1))
+    o, a, r, span, ta, tw = oracle.attention_spread(q, k, v, 0.5, window=(3, 1), tail_binades=0.5)
     np.testing.assert_array_equal(o, oracle.attention(q, k, v, 0.5, window=(3, 1)))
+    assert (ta <= a + 1e-15).all() and (tw <= 1.0).all() and tw.any()
     rows = np.array([5, 0, 71, 33])
-    o2, a2, r2, s2 = oracle.attention_spread(q, k, v, 0.5, window=(3, 1), rows=rows)
+    o2, a2, r2, s2, ta2, tw2 = oracle.attention_spread(q, k, v, 0.5, window=(3, 1), rows=rows, tail_binades=0.5)
+    np.testing.assert_array_equal(ta2, ta.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(tw2, tw.reshape(-1)[rows])
     np.testing.assert_array_equal(o2, o.reshape(-1, 8)[rows])
     np.testing.assert_array_equal(a2, a.reshape(-1, 8)[rows])
     np.testing.assert_array_equal(r2, r.reshape(-1, 8)[rows])
