@@ -92,10 +92,12 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
         if w.dtype == "e4m3":
             out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-            info["compute"] = "Q K^T on FP8 E4M3 MFMA, P V on f16 MFMA, fp32 accumulation, bf16 out"
+            info["compute"] = ("Q K^T and P V (E4M3 probabilities, E4M3 V) on FP8 E4M3 MFMA, fp32 accumulation, "
+                               "bf16 out" if w.fp8_probs else
+                               "Q K^T on FP8 E4M3 MFMA, P V on f16 MFMA, fp32 accumulation, bf16 out")
 
             def step():
-                binding.attn_forward_fp8(q, k, v, out, w.scale, w.causal)
+                binding.attn_forward_fp8(q, k, v, out, w.scale, w.causal, fp8_probs=w.fp8_probs)
             return w, step, step, info, (q, k, v)
         out = torch.empty_like(q)
         if w.attn_window is not None:
@@ -198,7 +200,7 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         c = state["c"]
         q, k, v = sets[c % nsets]
         binding.stream_self_attention_step(cache, c, q, k, v, q_buf, out, gq, gk, angles[min(c, 7)], 1e-6, w.scale,
-                                           workspace=ws)
+                                           workspace=ws, fp8_probs=w.fp8_probs)
         state["c"] = c + 1
 
     for _ in range(S // Lc):  # fill the cache before timing
@@ -213,9 +215,9 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
     def kern():
         keys = cache.k_rot if after else cache.k
         if ws is not None:
-            binding.attn_forward_ws(q_buf, keys, cache.v, out, w.scale, ws, Lk=S)
+            binding.attn_forward_ws(q_buf, keys, cache.v, out, w.scale, ws, Lk=S, fp8_probs=w.fp8_probs)
         else:
-            binding.attn_forward_kvstride(q_buf, keys, cache.v, out, S, w.scale, False)
+            binding.attn_forward_kvstride(q_buf, keys, cache.v, out, S, w.scale, False, fp8_probs=w.fp8_probs)
 
     # the HBM-bound steps alone, on rotating input sets, query buffers and cache slots (each input
     # set is read once per 10 calls; outputs go to one of 4 query buffers and one of the cache's
@@ -450,7 +452,7 @@ def main():
 
     flops = workload_flops(w)
     fp8 = w.dtype == "e4m3" or w.cache_dtype == "e4m3"
-    peak = PEAK_MFMA_FP8_F16 if fp8 else PEAK_MFMA_16BIT
+    peak = PEAK_MFMA_FP8 if w.fp8_probs else PEAK_MFMA_FP8_F16 if fp8 else PEAK_MFMA_16BIT
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kern * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
@@ -475,7 +477,7 @@ def main():
                                "right after the timed steps"}),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"attn_fwd_kernel<{w.d},{'e4m3' if fp8 else w.dtype}>",
+                     "kernel": f"attn_fwd_kernel<{w.d},{('e4m3p8' if w.fp8_probs else 'e4m3') if fp8 else w.dtype}>",
                      "kernel_ms": round(ms_kern, 4)},
         "cpu_baseline": None,
     }

@@ -14,7 +14,7 @@ import torch
 
 from . import build as _build
 
-SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3, SA_DTYPE_BF16_F16V = 0, 1, 2, 3
+SA_DTYPE_BF16, SA_DTYPE_F16, SA_DTYPE_FP8_E4M3, SA_DTYPE_BF16_F16V, SA_DTYPE_FP8_E4M3_P8 = 0, 1, 2, 3, 4
 SA_ERR_SHAPE_CODE, SA_ERR_UNSUPPORTED_CODE = -2, -3
 SA_NORM_NONE, SA_NORM_HEAD, SA_NORM_INNER = 0, 1, 2
 SA_ROPE_NONE, SA_ROPE_SPLIT, SA_ROPE_INTERLEAVED, SA_ROPE_AFTER_CACHE = 0, 1, 2, 4
@@ -102,13 +102,20 @@ def _require_bf16(fn: str, *tensors) -> None:
             raise StreamAttnError(fn, SA_ERR_UNSUPPORTED_CODE, f"inputs must be bfloat16, got {t.dtype}")
 
 
-def _attn_dtype(q, k, v) -> int:
-    """Attention dtype code of (q, k, v): one common type, or bf16 q/k with an f16 v."""
+def _attn_dtype(q, k, v, fp8_probs: bool = False) -> int:
+    """Attention dtype code of (q, k, v): one common type, or bf16 q/k with an f16 v; with
+    fp8_probs (E4M3 q, k, v only) the opt-in FP8-probability P*V."""
     if q.dtype == torch.bfloat16 and k.dtype == torch.bfloat16 and v.dtype == torch.float16:
-        return SA_DTYPE_BF16_F16V
-    if not (q.dtype == k.dtype == v.dtype):
+        code = SA_DTYPE_BF16_F16V
+    elif not (q.dtype == k.dtype == v.dtype):
         raise TypeError(f"unsupported attention dtypes {q.dtype}, {k.dtype}, {v.dtype}")
-    return _dtype_code(q)
+    else:
+        code = _dtype_code(q)
+    if fp8_probs:
+        if code != SA_DTYPE_FP8_E4M3:
+            raise TypeError("FP8 probabilities need float8_e4m3fn q, k and v")
+        return SA_DTYPE_FP8_E4M3_P8
+    return code
 
 
 def attn_forward(q, k, v, out, scale: float, causal: bool = False):
@@ -129,20 +136,22 @@ def attn_forward_f16(q, k, v, out, scale: float, causal: bool = False):
     return out
 
 
-def attn_forward_fp8(q, k, v, out, scale: float, causal: bool = False):
-    """FP8 attention: q, k, v float8_e4m3fn (contiguous), out bf16 [B, Lq, Hq, d]."""
-    return attn_forward_kvstride(q, k, v, out, k.shape[1], scale, causal)
+def attn_forward_fp8(q, k, v, out, scale: float, causal: bool = False, fp8_probs: bool = False):
+    """FP8 attention: q, k, v float8_e4m3fn (contiguous), out bf16 [B, Lq, Hq, d]. fp8_probs=True
+    also rounds the softmax probabilities to E4M3 for an FP8 P*V product (opt-in, less accurate)."""
+    return attn_forward_kvstride(q, k, v, out, k.shape[1], scale, causal, fp8_probs=fp8_probs)
 
 
-def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = False):
+def attn_forward_kvstride(q, k, v, out, Lk: int, scale: float, causal: bool = False, fp8_probs: bool = False):
     """Attention over the first Lk tokens of k, v [B, S, Hkv, d] (S >= Lk), e.g. a rolling cache.
-    bf16/f16 tensors, or float8_e4m3fn q, k, v with a bf16 out."""
+    bf16/f16 tensors, or float8_e4m3fn q, k, v with a bf16 out (fp8_probs: FP8 P*V)."""
     B, Lq, Hq, d = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     kv_bstride = S * Hkv * d
     _check("attn_forward_kvstride",
            lib().attn_forward_kvstride(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, int(Lk), d,
-                                       float(scale), int(bool(causal)), kv_bstride, _attn_dtype(q, k, v), _stream(q)))
+                                       float(scale), int(bool(causal)), kv_bstride, _attn_dtype(q, k, v, fp8_probs),
+                                       _stream(q)))
     return out
 
 
@@ -154,7 +163,8 @@ def attn_workspace(d: int, device=None) -> torch.Tensor:
     return torch.empty((int(n),), dtype=torch.uint8, device=device or "cuda")
 
 
-def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None, window=(-1, -1)):
+def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None, window=(-1, -1),
+                    fp8_probs: bool = False):
     """Attention over the first Lk tokens of k, v [B, S, Hkv, d] with a workspace (attn_workspace)
     that lets under-filled grids run balanced; same results as attn_forward_kvstride."""
     B, Lq, Hq, d = q.shape
@@ -162,12 +172,14 @@ def attn_forward_ws(q, k, v, out, scale: float, workspace, Lk: int | None = None
     left, right = (int(x) for x in window)
     _check("attn_forward_ws",
            lib().attn_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
-                                 d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _ptr(workspace),
+                                 d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v, fp8_probs),
+                                 _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
     return out
 
 
-def attn_forward_ws_static(q, k, v, out, scale: float, Lk: int | None = None, window=(-1, -1)):
+def attn_forward_ws_static(q, k, v, out, scale: float, Lk: int | None = None, window=(-1, -1),
+                           fp8_probs: bool = False):
     """attn_forward_ws with the library's own per-GPU scratch instead of a workspace: allocates
     nothing. Calls that overlap on one GPU race (they share that scratch)."""
     B, Lq, Hq, d = q.shape
@@ -176,7 +188,7 @@ def attn_forward_ws_static(q, k, v, out, scale: float, Lk: int | None = None, wi
     _check("attn_forward_ws_static",
            lib().attn_forward_ws_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq,
                                         S if Lk is None else int(Lk), d, float(scale), left, right, S * Hkv * d,
-                                        _attn_dtype(q, k, v), _stream(q)))
+                                        _attn_dtype(q, k, v, fp8_probs), _stream(q)))
     return out
 
 
@@ -199,7 +211,8 @@ def attn_forward_qnorm(q, k, v, out, scale: float, gamma_q, eps: float = 1e-6, w
     return out
 
 
-def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk: int | None = None):
+def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk: int | None = None,
+                        fp8_probs: bool = False):
     """Local attention: query i (key position p = i + Lk - Lq) sees keys [p - left, p + right].
 
     window = (left, right), -1 for an unbounded side; k, v [B, S, Hkv, d] with S >= Lk
@@ -210,7 +223,8 @@ def attn_forward_window(q, k, v, out, scale: float, window: tuple[int, int], Lk:
     left, right = (int(w) for w in window)
     _check("attn_forward_window",
            lib().attn_forward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Lq, S if Lk is None else int(Lk),
-                                     d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v), _stream(q)))
+                                     d, float(scale), left, right, S * Hkv * d, _attn_dtype(q, k, v, fp8_probs),
+                                     _stream(q)))
     return out
 
 
@@ -435,7 +449,7 @@ def _check_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, ou
 def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, v_in, q_buf, out, gamma_q,
                                gamma_k, angles, eps: float, scale: float,
                                rope_style: int = SA_ROPE_SPLIT, norm_scope: int = SA_NORM_HEAD, workspace=None,
-                               query_in_attention: bool = False):
+                               query_in_attention: bool = False, fp8_probs: bool = False):
     """One streaming self-attention chunk as library calls between before_update / after_update.
 
     Default route: qk_norm_rope_v in one launch writes the normalised (and rotated, unless
@@ -458,7 +472,8 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
     stored unrotated; kv_cache_rope then rotates the visible keys into cache.k_rot, which the
     attention reads.
     workspace (attn_workspace): lets the attention run balanced when its grid would leave CU
-    slots idle. Returns the visible length used.
+    slots idle. fp8_probs (FP8 cache only, opt-in): the attention also rounds its softmax
+    probabilities to E4M3 for an FP8 P*V product. Returns the visible length used.
     """
     in_attn = (query_in_attention and norm_scope == SA_NORM_HEAD and cache.k.dtype == torch.bfloat16 and
                cache.v.dtype == torch.bfloat16)
@@ -492,9 +507,9 @@ def stream_self_attention_step(cache: BlockKVCache, chunk_idx: int, q_in, k_in, 
         attn_forward_qnorm(q_in, keys, cache.v, out, scale, gamma_q, eps, workspace=workspace, Lk=visible,
                            rope_cs=cache.rope_cs if rope else None, rope_style=rope_style)
     elif workspace is not None:
-        attn_forward_ws(q_buf, keys, cache.v, out, scale, workspace, Lk=visible)
+        attn_forward_ws(q_buf, keys, cache.v, out, scale, workspace, Lk=visible, fp8_probs=fp8_probs)
     else:
-        attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False)
+        attn_forward_kvstride(q_buf, keys, cache.v, out, visible, scale, False, fp8_probs=fp8_probs)
     cache.after_update(chunk_idx)
     return visible
 

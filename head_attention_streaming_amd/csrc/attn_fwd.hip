@@ -42,13 +42,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Input element types (template parameter DT): bf16 or f16 (output in the same type), FP8 E4M3
 // (OCP float8_e4m3fn, one byte; output bf16), or bf16 Q/K/out with f16 V (a cache that keeps V
 // in the type the P*V product uses, so no tile is converted).
-constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2, kDtBF16VF16 = 3;
+// FP8P: FP8 E4M3 q, k, v as kDtFP8, and the probabilities rounded to E4M3 for an FP8 P*V product
+// with V kept in E4M3 (the quantized-SDPA option's FP8 softmax probabilities; opt-in).
+constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2, kDtBF16VF16 = 3, kDtFP8P = 4;
 
 struct KParams {
     const void* q;  // [B, Lq, Hq, D] of the input type; strides below are in its elements
@@ -182,7 +186,8 @@ __device__ __forceinline__ int64_t w_begin(const KParams& p, int w) { return p.s
 
 template <int D, int DT, int NW, int KS, bool SK, bool BIG>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
-    constexpr bool FP8 = DT == kDtFP8;
+    constexpr bool P8 = DT == kDtFP8P;                 // E4M3 probabilities and V in P*V
+    constexpr bool FP8 = DT == kDtFP8 || P8;           // E4M3 q, k, v
     constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16;  // bf16 Q and K
     constexpr bool V_BF16 = DT == kDtBF16;                     // bf16 V, converted to f16 when staged
     constexpr bool OUT_BF16 = DT != kDtF16;                    // bf16 output
@@ -213,7 +218,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // separate arrays so every LDS offset stays within the 16-bit immediate of ds_read/ds_write.
     constexpr int kKSlot = kBN * KST, kVSlot = kBN * VST;
     __shared__ __attribute__((aligned(16))) In Ks[KS][2 * kKSlot];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[KS][2 * kVSlot];
+    // V tiles: f16 (converted from bf16 or E4M3 when staged), or the E4M3 bytes themselves for P8
+    // (row stride D + 32 bytes: the transposed byte reads of eight rows then hit every bank once)
+    using VT = std::conditional_t<P8, uint8_t, uint16_t>;
+    __shared__ __attribute__((aligned(16))) VT Vs[KS][2 * kVSlot];
     // Output rows leave through LDS (see the epilogue): one area of 32 rows per row wave, waves
     // [0, kRW/2) in the K tile array and the others in the V tile array, when they fit.
     constexpr int OST = D + 8;         // LDS row stride of the output block (elements)
@@ -337,9 +345,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                                                   (int)(uint32_t)bytes, kBufferWord3);
     };
     In* const Kg = &Ks[ks][0];  // this group's K and V slots (V always f16 in LDS)
-    uint16_t* const Vg = &Vs[ks][0];
+    VT* const Vg = &Vs[ks][0];
     In* ks_st = Kg + srow0 * KST + scol;
-    uint16_t* vs_st = Vg + srow0 * VST + scol;
+    VT* vs_st = Vg + srow0 * VST + scol;
     u32x4 kreg[NCH], vreg[NCH];
     auto load_rows = [&](u32x4 (&dst)[NCH], const char* base, const __amdgpu_buffer_rsrc_t& whole, int kt)
                          __attribute__((always_inline)) {
@@ -367,8 +375,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     auto store_v = [&](int slot) __attribute__((always_inline)) {
         if (!stager) return;
         static_for<NCH>([&](auto u) __attribute__((always_inline)) {
-            uint16_t* dst = vs_st + slot * (kBN * VST) + u * RSTEP * VST;
-            if constexpr (FP8) {
+            VT* dst = vs_st + slot * (kBN * VST) + u * RSTEP * VST;
+            if constexpr (P8) {
+                *reinterpret_cast<u32x4*>(dst) = vreg[u];
+            } else if constexpr (FP8) {
                 u32x4 lo, hi;
                 fp8x16_to_f16x16(vreg[u], lo, hi);
                 *reinterpret_cast<u32x4*>(dst) = lo;
@@ -466,18 +476,30 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 
     // LDS read addresses (address space 3, so constant offsets fold into the instructions).
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
-    lds_u4* kq_lane = (lds_u4*)(Kg + j * KST + (FP8 ? 32 : 8) * g);
+    // P8 reads the K rows of each 32-key block in the order 8a + 4b + c -> key 16(a >> 1) + 8b +
+    // 4(a & 1) + c, so that score registers 0-7 (8-15) of lane half g hold the 8 consecutive keys
+    // 8g + [0, 8) (16 + 8g + [0, 8)): the runs the transposed byte reads of V deliver.
+    const int krow = P8 ? 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j >> 3) & 1) + (j & 3) : j;
+    lds_u4* kq_lane = (lds_u4*)(Kg + krow * KST + (FP8 ? 32 : 8) * g);
     // V^T operand addressing for ds_read_b64_tr_b16: loader lane L (within its 16-lane group G)
     // reads 4 features of key row (L / 4); the transpose hands lane L the 4 keys of feature L.
     const int G = lane >> 4, L16 = lane & 15;
     lds_i16x4* v_lane = (lds_i16x4*)(Vg + (4 * (G >> 1) + (L16 >> 2)) * VST + 16 * (G & 1) + 4 * (L16 & 3));
+    // P8: ds_read_b64_tr_b8 -- loader lane L of a 16-lane group reads 8 bytes of key row L / 2 at
+    // byte 8 (L % 2); lane i then holds byte i of those 8 rows (measured on the device). Group G
+    // reads the keys of lane half g = G / 2 and features 16 (G % 2) + [0, 16) of a 32-feature block.
+    lds_i32x2* v8_lane = (lds_i32x2*)((const uint8_t*)Vg + (8 * (G >> 1) + (L16 >> 1)) * VST + 16 * (G & 1) +
+                                      8 * (L16 & 1));
 
     const float c = p.c;
     // Running maximum used as the exponent offset (log2 domain). It is raised only when a
     // tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip the O rescale;
     // probabilities then stay below 2^kRescaleSlack, well inside f16 range. Finite start value,
     // so exp2 never sees inf - inf.
-    constexpr float kRescaleSlack = 8.0f;
+    // P8 rounds the probabilities to E4M3 (largest 448), so it raises m with every new maximum and
+    // offsets the exponent by 8: p = 2^(s c - m + 8) <= 2^8, normal down to 14 binades below m.
+    constexpr float kRescaleSlack = P8 ? 0.0f : 8.0f;
+    constexpr float kPOff = P8 ? 8.0f : 0.0f;
     float m_run = -1e30f;
     float l_run = 0.f;  // this lane's share of the row sum (its own keys)
     f32x16 o[DB];
@@ -487,6 +509,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
     f32x16 s0[KB], s1[KB];  // scores of tile t live in s[t & 1]
     u32x4 pf[KC];           // f16 probabilities of the previous tile (P^T operands)
+    i32x8 pf8;              // P8: the previous tile's E4M3 probabilities (one 64-key P^T operand)
 
     // One pipeline step t:  S(t) = K(t) Q^T  ||  P(t-1) = exp2(S(t-1) c - m)  [MFMA || VALU]
     //                       O += V(t-1) P(t-1)  ||  stage K(t+1), V(t); row max of S(t)
@@ -549,7 +572,30 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (PV && !pv_dead) {
+        if (P8 && PV && !pv_dead) {
+            // P(t-1) as E4M3: dword w holds contraction index 4w .. 4w + 3, i.e. score registers
+            // (kb, r) = (w / 4, 4 (w % 4) + e); the row sum adds the rounded values (widened
+            // exactly to f16 pairs) that the product uses
+            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            const float mo = m_run - kPOff;
+            float acc0 = 0.f, acc1 = 0.f;
+            int pw[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const int kb = w >> 2, r0 = 4 * (w & 3);
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][r0 + e], c, -mo));
+                int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                v = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
+                pw[w] = v;
+                acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, fp8x2_lo_to_f16x2((uint32_t)v)), one2, acc0, false);
+                acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, fp8x2_hi_to_f16x2((uint32_t)v)), one2, acc1, false);
+            }
+            pf8 = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+            l_run += acc0 + acc1;
+        }
+        if (!P8 && PV && !pv_dead) {
             // P(t-1) as f16 operands; the row sum adds the f16 values the product uses
             const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
             float acc0 = 0.f, acc1 = 0.f;
@@ -577,7 +623,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             load_k(min(t + 2, nkt - 1));
             load_v(min(t + 1, nkt - 1));
         }
-        if (PV && !pv_dead) {
+        if (P8 && PV && !pv_dead) {
+            // O^T += V^T P^T on the FP8 MFMA, 64 keys per product: read m of a 32-feature block
+            // brings keys 8 (2m + g) + [0, 8) of this lane's feature
+            const int slot = (t - 1) & 1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                i32x2 r[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    r[m] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(v8_lane + (slot * kBN * VST + 16 * m * VST + 32 * db) / 8);
+                const i32x8 va = {r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+                o[db] = mfma_qk_fp8(va, pf8, o[db]);
+            }
+        }
+        if (!P8 && PV && !pv_dead) {
             const int slot = (t - 1) & 1;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
@@ -594,12 +654,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         if (QK && !qk_dead) {
             if constexpr (MASK) {
                 // one unsigned compare and a select per score: key - key_lo in [0, key_span]
-                const int rel0 = t * kBN + 4 * g - key_lo;
+                // key of score register (kb, r) in lane half g: kb 32 + 8 (r / 4) + 4 g + r % 4, or
+                // with P8's row order kb 32 + 8 g + r + 8 (r / 8)
+                const int rel0 = t * kBN + (P8 ? 8 : 4) * g - key_lo;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const unsigned rel = (unsigned)(rel0 + kb * 32 + 8 * (r >> 2) + (r & 3));
+                        const unsigned rel = (unsigned)(rel0 + kb * 32 + (P8 ? r + 8 * (r >> 3) : 8 * (r >> 2) + (r & 3)));
                         sc[kb][r] = rel <= key_span ? sc[kb][r] : -INFINITY;
                     }
             }
@@ -1030,7 +1092,7 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // 4-wave workgroups: 8 waves per workgroup stage each tile once for twice the rows.
     // K/V regions whose rows up to one tile past Lk span 4 GiB or more: the plain 8-wave shape
     // with per-tile buffer resources (any grid)
-    const int64_t elem = DT == kDtFP8 ? 1 : 2;
+    const int64_t elem = DT == kDtFP8 || DT == kDtFP8P ? 1 : 2;
     if (((int64_t)a.Lk + 64) * a.Hkv * D * elem > 0xffffffffLL) return launch<D, DT, 8, 1, true>(a, stream);
     const int64_t cus = device_cu_count();
     const int64_t wg256 = (int64_t)((a.Lq + 255) / 256) * a.Hq * a.B;
@@ -1086,10 +1148,12 @@ hipError_t attn_scratch(void** out) {
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 128) {
         if (a.dtype == kDtFP8) return launch_shape<128, kDtFP8>(a, stream);
+        if (a.dtype == kDtFP8P) return launch_shape<128, kDtFP8P>(a, stream);
         if (a.dtype == kDtBF16VF16) return launch_shape<128, kDtBF16VF16>(a, stream);
         return a.dtype == kDtBF16 ? launch_shape<128, kDtBF16>(a, stream) : launch_shape<128, kDtF16>(a, stream);
     }
     if (a.dtype == kDtFP8) return launch_shape<64, kDtFP8>(a, stream);
+    if (a.dtype == kDtFP8P) return launch_shape<64, kDtFP8P>(a, stream);
     if (a.dtype == kDtBF16VF16) return launch_shape<64, kDtBF16VF16>(a, stream);
     return a.dtype == kDtBF16 ? launch_shape<64, kDtBF16>(a, stream) : launch_shape<64, kDtF16>(a, stream);
 }

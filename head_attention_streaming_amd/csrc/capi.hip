@@ -48,9 +48,11 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lq < 0 || Lk < 0)
         return fail(SA_ERR_RANGE, "attn_forward: negative or zero size (B=%d Hq=%d Hkv=%d Lq=%d Lk=%d)", B, Hq,
                     Hkv, Lq, Lk);
-    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16 && dtype != SA_DTYPE_FP8_E4M3 && dtype != SA_DTYPE_BF16_F16V)
-        return fail(SA_ERR_UNSUPPORTED, "attn_forward: dtype %d is not bf16 (0), f16 (1), fp8 e4m3 (2) or bf16 with f16 v (3)",
-                    dtype);
+    if (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F16 && dtype != SA_DTYPE_FP8_E4M3 && dtype != SA_DTYPE_BF16_F16V &&
+        dtype != SA_DTYPE_FP8_E4M3_P8)
+        return fail(SA_ERR_UNSUPPORTED,
+                    "attn_forward: dtype %d is not bf16 (0), f16 (1), fp8 e4m3 (2), bf16 with f16 v (3) or fp8 e4m3 with "
+                    "fp8 probabilities (4)", dtype);
     if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "attn_forward: head dim %d not built (64, 128)", d);
     if (Hq % Hkv != 0) return fail(SA_ERR_SHAPE, "attn_forward: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (win_left < -1 || win_right < -1)
@@ -72,7 +74,7 @@ int check_attn(const void* q, const void* k, const void* v, void* out, int B, in
         return fail(SA_ERR_RANGE, "attn_forward: tensor too large");
     if (kv_bstride < nkv) return fail(SA_ERR_SHAPE, "attn_forward: kv_bstride %lld < Lk*Hkv*d %lld",
                                       (long long)kv_bstride, (long long)nkv);
-    const int elem_bytes = dtype == SA_DTYPE_FP8_E4M3 ? 1 : 2;
+    const int elem_bytes = dtype == SA_DTYPE_FP8_E4M3 || dtype == SA_DTYPE_FP8_E4M3_P8 ? 1 : 2;
     if ((kv_bstride * elem_bytes) % 16)
         return fail(SA_ERR_ALIGN, "attn_forward: kv_bstride must be a multiple of 16 bytes");
     if (mul4(B, kv_bstride, 1, 1) < 0) return fail(SA_ERR_RANGE, "attn_forward: K/V extent overflows");
@@ -187,7 +189,7 @@ int attn_forward_qnorm(const void* q, const void* k, const void* v, void* out, c
     if (!gamma_q) return fail(SA_ERR_NULL, "attn_forward_qnorm: gamma_q is null");
     if (!aligned16(gamma_q)) return fail(SA_ERR_ALIGN, "attn_forward_qnorm: gamma_q must be 16-byte aligned");
     if (!(eps >= 0.f) || eps > 1e30f) return fail(SA_ERR_RANGE, "attn_forward_qnorm: eps must be >= 0 and finite");
-    if (dtype == SA_DTYPE_FP8_E4M3)
+    if (dtype == SA_DTYPE_FP8_E4M3 || dtype == SA_DTYPE_FP8_E4M3_P8)
         return fail(SA_ERR_UNSUPPORTED, "attn_forward_qnorm: the fused query norm takes 16-bit queries");
     if (rope_style != SA_ROPE_NONE && rope_style != SA_ROPE_SPLIT && rope_style != SA_ROPE_INTERLEAVED)
         return fail(SA_ERR_UNSUPPORTED, "attn_forward_qnorm: unknown RoPE pairing %d", rope_style);

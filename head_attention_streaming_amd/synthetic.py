@@ -84,6 +84,7 @@ class Workload:
     rope_scope: str = "before"        # streaming: RoPE before or after the K/V cache update
     cache_dtype: str = "bf16"         # streaming: element type of the K/V cache and attention inputs
     v_cache_dtype: str | None = None  # V kept in another type (f16: the type P*V uses), same results
+    fp8_probs: bool = False           # e4m3: softmax probabilities rounded to E4M3 for an FP8 P*V
 
     @property
     def flops(self) -> float:
@@ -130,6 +131,12 @@ WORKLOADS = {
     # the long problem with unscaled FP8 E4M3 q, k, v (bf16 out)
     "mha_20480_fp8": Workload("mha_20480_fp8", 1, 56, 56, 20480, 20480, 128, "e4m3", False,
                               128 ** -0.5, 1005),
+    # the same two with the probabilities also rounded to E4M3 for an FP8 P*V product (opt-in)
+    "mha_20480_fp8p": Workload("mha_20480_fp8p", 1, 56, 56, 20480, 20480, 128, "e4m3", False,
+                               128 ** -0.5, 1005, fp8_probs=True),
+    "stream_fp8p_1785x4": Workload("stream_fp8p_1785x4", 1, 40, 40, 1785, 7140, 128, "bf16", False,
+                                   128 ** -0.5, 1300, "qk_norm_rope", 1785, 7140, cache_dtype="e4m3",
+                                   fp8_probs=True),
     # sliding-window (local) attention, [4, 4096, 32, 64] fp16, 256 keys back + the query's own
     "window_4096_w256_f16": Workload("window_4096_w256_f16", 4, 32, 32, 4096, 4096, 64, "f16", False,
                                      0.125, 1006, attn_window=(256, 0)),

@@ -426,3 +426,16 @@ def test_block_kv_cache_lifecycle_order_and_reset():
     with pytest.raises(binding.StreamAttnError):
         cache.before_update(2)
     assert cache.before_update(0) == (0, 4)
+
+
+def test_fp8_probability_dtype_is_accepted_and_qnorm_rejects_it():
+    """dtype 4 (E4M3 with FP8 probabilities) passes validation like dtype 2 (an empty problem is a
+    no-op), needs 16-byte K/V batch strides in bytes, and the fused query norm rejects it."""
+    lib = binding.lib()
+    p = ctypes.c_void_p(4096)
+    assert lib.attn_forward_kvstride(p, p, p, p, 0, 8, 8, 16, 16, 128, 0.1, 0, 16 * 8 * 128, 4, None) == 0
+    assert lib.attn_forward_kvstride(p, p, p, p, 1, 8, 8, 16, 16, 128, 0.1, 0, 16 * 8 * 128 + 8, 4, None) == -4
+    assert lib.attn_forward_kvstride(p, p, p, p, 1, 8, 8, 16, 16, 128, 0.1, 0, 16 * 8 * 128, 5, None) == -3
+    g = ctypes.c_void_p(8192)
+    assert lib.attn_forward_qnorm(p, p, p, p, g, 1e-6, None, 0, 1, 8, 8, 16, 16, 128, 0.1, -1, -1, 16 * 8 * 128, 4,
+                                  None, 0, None) == -3
