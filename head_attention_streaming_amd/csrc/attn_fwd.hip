@@ -52,7 +52,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // in the type the P*V product uses, so no tile is converted).
 // FP8P: FP8 E4M3 q, k, v as kDtFP8, and the probabilities rounded to E4M3 for an FP8 P*V product
 // with V kept in E4M3 (the quantized-SDPA option's FP8 softmax probabilities; opt-in).
-constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2, kDtBF16VF16 = 3, kDtFP8P = 4;
+// BF16P (chosen by the launch, not an ABI type): bf16 q, k, v with the probabilities rounded to
+// bf16 for a bf16 P*V product, V staged as is -- for rows that all see at least
+// kBf16ProbMinKeys keys, where the rounding averages out well inside the output bounds.
+constexpr int kDtBF16 = 0, kDtF16 = 1, kDtFP8 = 2, kDtBF16VF16 = 3, kDtFP8P = 4, kDtBF16P = 5;
 
 struct KParams {
     const void* q;  // [B, Lq, Hq, D] of the input type; strides below are in its elements
@@ -188,7 +191,8 @@ template <int D, int DT, int NW, int KS, bool SK, bool BIG>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr bool P8 = DT == kDtFP8P;                 // E4M3 probabilities and V in P*V
     constexpr bool FP8 = DT == kDtFP8 || P8;           // E4M3 q, k, v
-    constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16;  // bf16 Q and K
+    constexpr bool PB = DT == kDtBF16P;                        // bf16 probabilities and V in P*V
+    constexpr bool BF16 = DT == kDtBF16 || DT == kDtBF16VF16 || PB;  // bf16 Q and K
     constexpr bool V_BF16 = DT == kDtBF16;                     // bf16 V, converted to f16 when staged
     constexpr bool OUT_BF16 = DT != kDtF16;                    // bf16 output
     using In = std::conditional_t<FP8, uint8_t, uint16_t>;
@@ -607,11 +611,20 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e], c, -m_run));
                     const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e + 1], c, -m_run));
-                    w[e] = pack_f16x2(x0, x1);
-                    if (e & 1)
-                        acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc1, false);
-                    else
-                        acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc0, false);
+                    if constexpr (PB) {
+                        w[e] = pack_bf16x2(x0, x1);
+                        const bf16x2 one_b = {(__bf16)1.0f, (__bf16)1.0f};
+                        if (e & 1)
+                            acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc1, false);
+                        else
+                            acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc0, false);
+                    } else {
+                        w[e] = pack_f16x2(x0, x1);
+                        if (e & 1)
+                            acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc1, false);
+                        else
+                            acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc0, false);
+                    }
                 }
                 pf[kc] = u32x4{w[0], w[1], w[2], w[3]};
             }
@@ -647,8 +660,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                     const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off);
                     const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(v_lane + off + 2 * VST);
                     const i16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
-                                                                    __builtin_bit_cast(f16x8, pf[kc]), o[db], 0, 0, 0);
+                    if constexpr (PB)
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8),
+                                                                         __builtin_bit_cast(bf16x8, pf[kc]), o[db], 0, 0, 0);
+                    else
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
+                                                                        __builtin_bit_cast(f16x8, pf[kc]), o[db], 0, 0, 0);
                 }
         }
         if (QK && !qk_dead) {
@@ -1145,7 +1162,17 @@ hipError_t attn_scratch(void** out) {
     return hipSuccess;
 }
 
+// Every row of a full-range (no causal mask, no window) bf16 launch with at least this many keys
+// takes bf16 probabilities: each probability then carries a relative rounding error of at most
+// 2^-8 (zero-mean for independent mantissas), so the output error is a weighted sum of those
+// errors times (v_j - o), whose mean shrinks like 1/sqrt(keys): at 2048 keys it stays 2x below
+// the mean-abs bound on unit-variance data (and the worst case, 2^-8 / (1 - 2^-8) times the
+// weighted mean of |v_j - o|, below the max-abs bound). Shorter rows keep f16 probabilities.
+constexpr int kBf16ProbMinKeys = 2048;
+
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+    const bool bf16_probs = a.dtype == kDtBF16 && a.win_left < 0 && a.win_right < 0 && a.Lk >= kBf16ProbMinKeys;
+    if (bf16_probs) return a.d == 128 ? launch_shape<128, kDtBF16P>(a, stream) : launch_shape<64, kDtBF16P>(a, stream);
     if (a.d == 128) {
         if (a.dtype == kDtFP8) return launch_shape<128, kDtFP8>(a, stream);
         if (a.dtype == kDtFP8P) return launch_shape<128, kDtFP8P>(a, stream);

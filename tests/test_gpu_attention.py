@@ -262,3 +262,19 @@ def test_kv_regions_at_and_past_4gib(case):
         assert_attention_close(out[:, :, h:h + 1].contiguous(), ref, f"{name} head {h}")
     del q, k, v, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Lk", [2047, 2048, 4100])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_probability_threshold_rows(Lk, d):
+    """bf16 launches whose rows all see at least 2048 keys (no mask) round the probabilities to
+    bf16 for a bf16 P*V product; shorter rows keep f16 probabilities. Every row on both sides of
+    the threshold, against the oracle, within the standard bounds."""
+    B, Lq, H = 1, 300, 4
+    print(f"[case] Lk={Lk} d={d}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, H, H, d, "bf16", seed=2040 + Lk + d)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=DEV)
+    binding.attn_forward(q.to(DEV), k.to(DEV), v.to(DEV), out, d ** -0.5)
+    torch.cuda.synchronize()
+    Q, K, V = (widen(x).reshape(x.shape) for x in (q, k, v))
+    assert_attention_close(out, oracle.attention(Q, K, V, d ** -0.5), f"Lk={Lk} d={d}")
