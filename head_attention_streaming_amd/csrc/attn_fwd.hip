@@ -25,8 +25,22 @@
 
 #include "sa_internal.h"
 
+// SA_LDS_CHECK=1 builds a check variant of the kernels (a separate library, compared bit for bit
+// with the fast one by the tests): one LDS slot for K and one for V instead of two, each written
+// only after a barrier that follows every read of its previous tile, and V staged after the
+// P*V product that read the previous V. A barrier missing from the fast build's double-buffered
+// pipeline would let a wave read a tile being overwritten; the check variant cannot, so the two
+// builds' outputs would differ.
+#ifndef SA_LDS_CHECK
+#define SA_LDS_CHECK 0
+#endif
+
 namespace sa {
 namespace {
+
+constexpr bool kLdsCheck = SA_LDS_CHECK != 0;
+// LDS slot of key tile t: double buffering, or the single slot of the check variant
+__device__ __forceinline__ int lds_slot(int t) { return kLdsCheck ? 0 : (t & 1); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -536,7 +550,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 static_assert(NQ > kLook, "more products than reads in flight");
                 u32x4 kbuf[NQ];
                 auto kread = [&](int i) __attribute__((always_inline)) {
-                    kbuf[i] = kq_lane[((t & 1) * kBN * KST + (i / DC) * 32 * KST + 16 * (i % DC)) / 8];
+                    kbuf[i] = kq_lane[(lds_slot(t) * kBN * KST + (i / DC) * 32 * KST + 16 * (i % DC)) / 8];
                 };
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
@@ -564,12 +578,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
 #pragma unroll
                     for (int cc = 0; cc < DC; ++cc) {
                         if constexpr (FP8) {
-                            const int off = ((t & 1) * kBN * KST + kb * 32 * KST + 64 * cc) / 16;
+                            const int off = (lds_slot(t) * kBN * KST + kb * 32 * KST + 64 * cc) / 16;
                             const u32x4 lo = kq_lane[off], hi = kq_lane[off + 1];
                             sc[kb] = mfma_qk_fp8(__builtin_bit_cast(i32x8, (u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w})),
                                                  qf[cc], sc[kb]);
                         } else {
-                            sc[kb] = mfma_qk<BF16>(kq_lane[((t & 1) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
+                            sc[kb] = mfma_qk<BF16>(kq_lane[(lds_slot(t) * kBN * KST + kb * 32 * KST + 16 * cc) / 8], qf[cc], sc[kb]);
                         }
                     }
                 }
@@ -631,15 +645,16 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             l_run += acc0 + acc1;
         }
         if constexpr (QK) {
-            store_k((t + 1) & 1);  // K(t+1) (slot content unused when t + 1 == nkt)
-            store_v(t & 1);        // V(t)
+            if constexpr (kLdsCheck) __syncthreads();  // every wave has read K(t) from the one K slot
+            store_k(lds_slot(t + 1));  // K(t+1) (slot content unused when t + 1 == nkt)
+            if constexpr (!kLdsCheck) store_v(lds_slot(t));  // V(t)
             load_k(min(t + 2, nkt - 1));
-            load_v(min(t + 1, nkt - 1));
+            if constexpr (!kLdsCheck) load_v(min(t + 1, nkt - 1));
         }
         if (P8 && PV && !pv_dead) {
             // O^T += V^T P^T on the FP8 MFMA, 64 keys per product: read m of a 32-feature block
             // brings keys 8 (2m + g) + [0, 8) of this lane's feature
-            const int slot = (t - 1) & 1;
+            const int slot = lds_slot(t - 1);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 i32x2 r[4];
@@ -651,7 +666,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             }
         }
         if (!P8 && PV && !pv_dead) {
-            const int slot = (t - 1) & 1;
+            const int slot = lds_slot(t - 1);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -667,6 +682,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a8),
                                                                         __builtin_bit_cast(f16x8, pf[kc]), o[db], 0, 0, 0);
                 }
+        }
+        if constexpr (QK && kLdsCheck) {
+            __syncthreads();  // every wave has read V(t-1) from the one V slot
+            store_v(lds_slot(t));
+            load_v(min(t + 1, nkt - 1));
         }
         if (QK && !qk_dead) {
             if constexpr (MASK) {
@@ -720,7 +740,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     };
 
     if (nkt > t0) {  // uniform over the workgroup: every group runs nsteps + 1 steps
-        store_k(ta & 1);
+        store_k(lds_slot(ta));
         if constexpr (SK)
             load_k(min(ta + 1, nkt - 1));
         else
