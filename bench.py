@@ -263,6 +263,17 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
     }
     if one_launch:  # q, k, v read (bf16) + written (cache type), angles, gammas
         info["hbm_steps"]["qk_norm_rope_v"] = (prologue_v, 3 * elem + 3 * out_elem + Lc * (w.d // 2) * 4 + 2 * w.d * 4)
+        # the copy ceiling at this size: the plain 16-byte copy kernel moving the one-launch
+        # prologue's bytes (three chunks in, three out), over 5 rotating buffer pairs (550 MB)
+        cp_src = [torch.empty((w.B, 3 * Lc, w.Hq, w.d), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(5)]
+        cp_dst = [torch.empty_like(x) for x in cp_src]
+
+        def copy_same_bytes():
+            i = rot["i"]
+            rot["i"] = i + 1
+            binding.kv_cache_append(None, cp_src[i % 5], None, cp_dst[i % 5], 0, 0, 3 * Lc)
+        if w.cache_dtype == "bf16":
+            info["hbm_steps"]["copy_same_bytes"] = (copy_same_bytes, 6 * elem)
     if after:
         def cache_rope():
             binding.kv_cache_rope(cache.k, cache.k_rot, angles[7], state["c"] - 1, Lc, 0, S, binding.SA_ROPE_SPLIT)

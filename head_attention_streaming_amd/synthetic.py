@@ -95,6 +95,8 @@ class Workload:
 WORKLOADS = {
     # non-causal MHA, [1, 257, 8, 128] bf16, scale 1/sqrt(128)
     "mha_257_bf16": Workload("mha_257_bf16", 1, 8, 8, 257, 257, 128, "bf16", False, 128 ** -0.5, 1001),
+    # the same queries over 20 keys: a workgroup's fixed cost (one masked key tile, no loop)
+    "mha_257x20_bf16": Workload("mha_257x20_bf16", 1, 8, 8, 257, 20, 128, "bf16", False, 128 ** -0.5, 1001),
     # causal MHA, [2, 2048, 8, 64] fp16, scale 1/8
     "causal_2048_f16": Workload("causal_2048_f16", 2, 8, 8, 2048, 2048, 64, "f16", True, 0.125, 1002),
     # streaming self-attention: 40 heads, d 128, chunk 1785, rolling cache of 4 chunks (7140 keys)
