@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    f32x16 s0[KB], s1[KB];  // scores of tile t live in s[t & 1]
+    f32x16 s0[KB], s1[KB];  // scores of tile t live in s[(t - ta) & 1]
     u32x4 pf[KC];           // f16 probabilities of the previous tile (P^T operands)
     i32x8 pf8;              // P8: the previous tile's E4M3 probabilities (one 64-key P^T operand)
 
@@ -728,10 +728,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // steps t in [a, b) with both halves; S(t) lives in s0 for even t, s1 for odd t
-    auto middle = [&](auto do_mask, int ta, int t1) __attribute__((always_inline)) {
-        int t = ta;
-        if (t < t1 && (t & 1)) step(T_{}, T_{}, do_mask, t++, s1, s0);
+    // steps t in [a, b) with both halves; S(t) lives in s0 when t - ta is even, s1 when odd
+    auto middle = [&](auto do_mask, int a, int t1) __attribute__((always_inline)) {
+        int t = a;
+        if (t < t1 && ((t - ta) & 1)) step(T_{}, T_{}, do_mask, t++, s1, s0);
         for (; t + 1 < t1; t += 2) {
             step(T_{}, T_{}, do_mask, t, s0, s1);
             step(T_{}, T_{}, do_mask, t + 1, s1, s0);
@@ -747,13 +747,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             static_for<NCH>([&](auto u) __attribute__((always_inline)) { kreg[u] = knext[u]; });
         __syncthreads();
         const bool mask0 = ta < tl || ta >= tr;
-        if (ta & 1) {
-            if (mask0) step(T_{}, F_{}, T_{}, ta, s1, s0);
-            else step(T_{}, F_{}, F_{}, ta, s1, s0);
-        } else {
-            if (mask0) step(T_{}, F_{}, T_{}, ta, s0, s1);
-            else step(T_{}, F_{}, F_{}, ta, s0, s1);
-        }
+        if (mask0) step(T_{}, F_{}, T_{}, ta, s0, s1);
+        else step(T_{}, F_{}, F_{}, ta, s0, s1);
         // steps ta+1 .. tend-1 in three segments: left-edge masked, unmasked, right-edge masked.
         // A masked step also decides whether this wave skips the previous tile's softmax and
         // P*V, so when the tile before the unmasked run is masked, the run starts one step later
@@ -766,7 +761,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         middle(F_{}, e1, e2);
         middle(T_{}, e2, tend);
         const bool mlast = kSkipDead && masked(tend - 1);
-        if (tend & 1) {  // S(tend-1) in s0 when tend-1 is even
+        if ((tend - ta) & 1) {  // S(tend-1) in s0 when tend-1-ta is even
             if (mlast) step(F_{}, T_{}, T_{}, tend, s1, s0);
             else step(F_{}, T_{}, F_{}, tend, s1, s0);
         } else {
