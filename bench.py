@@ -452,7 +452,10 @@ def main():
     ms_step, wall_ms = time_loop(step, args.steps, 0)
     ms_kern, _ = time_loop(kern, args.steps, 2) if kern is not step else (ms_step, wall_ms)
 
-    clock = shader_clock_mhz(kern)
+    # The sampler reads the instantaneous clock: between the host submissions of launches much
+    # shorter than a millisecond the GPU idles and amd-smi reports idle clocks, so only long
+    # launches are sampled.
+    clock = shader_clock_mhz(kern) if ms_kern >= 1.0 else None
     hbm = {}
     for name, (fn, nbytes) in info.pop("hbm_steps", {}).items():
         ms_h, _ = time_loop(fn, args.steps, args.warmup)
@@ -485,7 +488,10 @@ def main():
                        shader_clock_mhz=None if clock is None else
                        {"mean": clock[0], "min": clock[1], "max": clock[2],
                         "how": "amd-smi metric -c, every XCD, read while the kernel ran back to back "
-                               "right after the timed steps"}),
+                               "right after the timed steps"},
+                       **({} if ms_kern >= 1.0 else
+                          {"shader_clock_note": "not sampled: launches under 1 ms leave the GPU idle "
+                                                "between host submissions, where amd-smi reads idle clocks"})),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": f"attn_fwd_kernel<{w.d},{('e4m3p8' if w.fp8_probs else 'e4m3') if fp8 else w.dtype}>",
