@@ -29,7 +29,7 @@ def _cases():
     Lq40 = -(-units // 40) * BM - 85              # 40 heads, ragged last query block
     Lq64 = -(-units // 64) * BM - 28
     return [
-        # name, B, Lq, Lk, Hq, Hkv, d, dtype; key loops of at least 32 tiles with a ragged last one
+        # name, B, Lq, Lk, Hq, Hkv, d, dtype; key loops of at least 16 tiles with a ragged last one
         ("bal_bf16_d128_ragged", 1, Lq40, 2100, 40, 40, 128, "bf16"),
         ("bal_f16_d64_gqa", 1, Lq64, 2100, 64, 16, 64, "f16"),
         ("bal_bf16_batch2", 2, -(-units // 80) * BM - 3, 2080, 40, 8, 128, "bf16"),
@@ -37,6 +37,9 @@ def _cases():
         # 4 surplus blocks of 33 tiles over CUs workgroups: most pieces are empty
         ("bal_sparse_surplus", 1, (cus // 4 + 1) * BM - 7, 2100, 4, 4, 128, "bf16"),
         ("bal_stream_shape", 1, 1785, 7140, 40, 40, 128, "bf16"),
+        # the shortest balanced key loops: 16 tiles (ragged), 24 tiles at d = 64
+        ("bal_bf16_16_tiles", 1, Lq40, 1000, 40, 40, 128, "bf16"),
+        ("bal_f16_d64_24_tiles", 1, Lq64, 1500, 64, 16, 64, "f16"),
     ]
 
 
@@ -53,7 +56,7 @@ def _split_rows(B, Lq, Hq):
     return np.array(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(8))
 def test_balanced_matches_oracle(idx):
     name, B, Lq, Lk, Hq, Hkv, d, dtype = _cases()[idx]
     print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype}", flush=True)

@@ -20,7 +20,7 @@ def _cases():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     units = cus + cus // 9 + 1   # just over one round of 256-row blocks: a balanced grid
     return [
-        # name, B, Lq, Lk, Hq, Hkv, d, dtype (key loops of at least 32 tiles of 64 keys)
+        # name, B, Lq, Lk, Hq, Hkv, d, dtype (key loops of at least 16 tiles of 64 keys)
         ("static_bf16_d128", 1, -(-units // 40) * BM - 85, 2100, 40, 40, 128, "bf16"),
         ("static_f16_d64_gqa_smaller", 1, -(-units // 64) * BM - 200, 1990, 64, 16, 64, "f16"),
     ], cus
