@@ -214,13 +214,18 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr int kRW = NW / KS;          // row waves per key group
     constexpr int kGThreads = kRW * 64;   // threads of one key group (they stage its tiles)
     constexpr int kBM = kRW * 32;         // query rows per workgroup
+    // Four key groups split 64-row blocks for balance (d = 64 only: their double-buffered
+    // 64-key tiles take 147 KB of LDS).
+    static_assert(KS != 4 || D == 64, "four key groups only at d = 64");
     constexpr int kBN = kTileKeys;
     constexpr int KB = kBN / 32;  // 32-key score blocks per tile
     constexpr int KC = kBN / 16;  // 16-key P*V chunks per tile
     // LDS row stride of a K tile (input elements): 16 bytes of padding keep the b128 reads of
     // 16 consecutive rows on distinct banks
     constexpr int KST = D + 16 / (int)sizeof(In);
-    constexpr int VST = D + 32;   // LDS row stride of a V tile: conflict-free transposed reads
+    // LDS row stride of a V tile: conflict-free transposed reads (D + 16 with four key groups,
+    // whose tiles would not fit the LDS otherwise)
+    constexpr int VST = KS == 4 ? D + 16 : D + 32;
     constexpr int DC = FP8 ? D / 64 : D / 16;  // QK MFMAs per 32-key block (64 or 16 features each)
     constexpr int DB = D / 32;    // 32-feature blocks of the O^T accumulator
     constexpr int CPR = D / EPC;  // 16-byte chunks per key row (global memory)
@@ -230,7 +235,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     static_assert(kChunks < kGThreads ? kGThreads % kChunks == 0 && kChunks % 64 == 0
                                       : NCH * kGThreads == kChunks,
                   "tile must split evenly over the key group (or over whole waves of it)");
-    static_assert(KS == 1 || KS == 2, "one or two key groups");
+    static_assert(KS == 1 || KS == 2 || KS == 4, "one, two or four key groups");
 
     // Each key group owns two K slots and two V slots (double buffering) in LDS. K and V are
     // separate arrays so every LDS offset stays within the 16-bit immediate of ds_read/ds_write.
@@ -295,7 +300,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // Key groups split [t0, nkt) into consecutive runs of nsteps tiles; every group runs the same
     // number of steps (they share the barriers), so the last group may step over tiles >= nkt:
     // those re-read the last tile and are masked out entirely (tr <= nkt).
-    const int nsteps = KS == 1 ? nkt - t0 : (nkt - t0 + 1) / 2;
+    const int nsteps = KS == 1 ? nkt - t0 : (nkt - t0 + KS - 1) / KS;
     const int ta = t0 + ks * nsteps;
     const int tend = KS == 1 ? nkt : ta + nsteps;
     // this lane's visible keys [key_lo, key_lo + key_span] (rows past Lq may get an empty or
@@ -546,7 +551,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 // order pinned for the scheduler (which otherwise waits on each read right
                 // before its MFMA). Measured +2-5 % at d = 64; at d = 128 it gains nothing and
                 // the extra registers cost the balanced launch 7-10 %.
-                constexpr int NQ = KB * DC, kLook = 4;
+                constexpr int NQ = KB * DC, kLook = NQ > 4 ? 4 : NQ - 1;
                 static_assert(NQ > kLook, "more products than reads in flight");
                 u32x4 kbuf[NQ];
                 auto kread = [&](int i) __attribute__((always_inline)) {
@@ -770,49 +775,67 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         }
     }
 
-    if constexpr (KS == 2) {
-        // Merge the two key groups' partial results through LDS (the tiles are no longer read:
-        // every step ended with a barrier): (m, l, O) = (max, l0 a0 + l1 a1, O0 a0 + O1 a1) with
-        // a_i = exp2(m_i - m). Group 1 hands over m and l through the K buffers and O through
-        // the V buffers, DBR 32-feature blocks per round; group 0 merges and stores.
-        constexpr int kPerDb = kRW * 16 * 64;  // floats of one 32-feature block, all row waves
-        constexpr int DBR = (int)(sizeof(Vs) / 4 / kPerDb) < DB ? (int)(sizeof(Vs) / 4 / kPerDb) : DB;
-        static_assert(DBR >= 1 && kRW * 128 * 4 <= (int)sizeof(Ks), "merge areas must fit in the tile buffers");
-        float* ml = reinterpret_cast<float*>(&Ks[0][0]) + rw * 128 + lane;
-        float* area = reinterpret_cast<float*>(&Vs[0][0]) + rw * (DBR * 16 * 64) + lane;
-        if (ks == 1) {
-            ml[0] = m_run;
-            ml[64] = l_run;
+    if constexpr (KS > 1) {
+        // Merge the key groups' partial results through LDS (the tiles are no longer read: every
+        // step ended with a barrier): (m, l, O) = (max_i m_i, sum_i l_i a_i, sum_i O_i a_i) with
+        // a_i = exp2(m_i - m). Groups 1 .. KS-1 hand over m and l through the K buffers and O
+        // through the V buffers, DBR 32-feature blocks per round; group 0 merges and stores.
+        constexpr int kOut = KS - 1;           // groups that hand over
+        constexpr int kPerDb = kRW * 16 * 64;  // floats of one 32-feature block, all row waves of a group
+        constexpr int kFit = (int)(sizeof(Vs) / 4 / (kPerDb * kOut));
+        constexpr int DBR = kFit < DB ? kFit : DB;
+        static_assert(DBR >= 1 && kOut * kRW * 128 * 4 <= (int)sizeof(Ks), "merge areas must fit in the tile buffers");
+        float* const ml_base = reinterpret_cast<float*>(&Ks[0][0]) + rw * 128 + lane;
+        float* const area_base = reinterpret_cast<float*>(&Vs[0][0]) + rw * (DBR * 16 * 64) + lane;
+        auto ml = [&](int g) __attribute__((always_inline)) { return ml_base + (g - 1) * kRW * 128; };
+        auto area = [&](int g) __attribute__((always_inline)) { return area_base + (g - 1) * kRW * (DBR * 16 * 64); };
+        if (ks > 0) {
+            ml(ks)[0] = m_run;
+            ml(ks)[64] = l_run;
         }
         __syncthreads();
-        float a0 = 1.f, a1 = 0.f;
+        float a0 = 1.f, ag[kOut];
         if (ks == 0) {
-            const float m1 = ml[0], l1 = ml[64];
-            const float mn = fmaxf(m_run, m1);
+            float mg[kOut], mn = m_run;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                mg[g - 1] = ml(g)[0];
+                mn = fmaxf(mn, mg[g - 1]);
+            }
             a0 = __builtin_amdgcn_exp2f(m_run - mn);
-            a1 = __builtin_amdgcn_exp2f(m1 - mn);
-            l_run = l_run * a0 + l1 * a1;
+            l_run *= a0;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                ag[g - 1] = __builtin_amdgcn_exp2f(mg[g - 1] - mn);
+                l_run += ml(g)[64] * ag[g - 1];
+            }
         }
 #pragma unroll
         for (int d0 = 0; d0 < DB; d0 += DBR) {
-            if (ks == 1) {
+            if (ks > 0) {
+                float* const mine = area(ks);
 #pragma unroll
                 for (int db = d0; db < d0 + DBR && db < DB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) area[((db - d0) * 16 + r) * 64] = o[db][r];
+                    for (int r = 0; r < 16; ++r) mine[((db - d0) * 16 + r) * 64] = o[db][r];
             }
             __syncthreads();
             if (ks == 0) {
 #pragma unroll
                 for (int db = d0; db < d0 + DBR && db < DB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + area[((db - d0) * 16 + r) * 64] * a1;
+                    for (int r = 0; r < 16; ++r) {
+                        float acc = o[db][r] * a0;
+#pragma unroll
+                        for (int g = 1; g < KS; ++g) acc += area(g)[((db - d0) * 16 + r) * 64] * ag[g - 1];
+                        o[db][r] = acc;
+                    }
             }
-            // the next round overwrites the area, and after the last round the output rows
+            // the next round overwrites the areas, and after the last round the output rows
             // pass through the same buffers
             if (d0 + DBR < DB || kLdsOut) __syncthreads();
         }
-        if (ks == 1) return;
+        if (ks > 0) return;
     }
 
     if constexpr (SK) {
@@ -1151,7 +1174,20 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     const bool full8 = wg256 >= cus && wg256 * 10 >= (wg256 + cus - 1) / cus * cus * 9;
     if (wg256 >= 4 * cus || (full8 && a.Lk >= 2048)) return launch<D, DT, 8, 1>(a, stream);
     const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
-    if (wg128 <= cus && a.Lk >= 512) return launch<D, DT, 8, 2>(a, stream);
+    if (wg128 <= cus && a.Lk >= 512) {
+        // d = 64, rows over at least 1024 keys with no left window edge: four key groups over
+        // 64-row blocks (twice the blocks, each group a quarter of the loop) when causal rows
+        // make the blocks' loops unequal -- dispatched longest first, a CU's second block is as
+        // short as its first was long, so the rounds even out without a merge across
+        // workgroups -- or when 128-row blocks would leave half the CUs idle. Measured on MI355X
+        // against the two-group shape: causal [2,1024,8,64] +20 %, [1,4096,8,64] +13 %,
+        // [2,2048,8,64] +2 %, non-causal [1,2048,4,64] +26 %; a (256, 0) window over the same
+        // grid -64 %, so banded rows keep two groups.
+        if constexpr (D == 64)
+            if (a.win_left < 0 && a.Lk >= 1024 && (a.win_right >= 0 || 2 * wg128 <= cus))
+                return launch<D, DT, 8, 4>(a, stream);
+        return launch<D, DT, 8, 2>(a, stream);
+    }
     return launch<D, DT, 4, 1>(a, stream);
 }
 

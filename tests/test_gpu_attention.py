@@ -164,8 +164,9 @@ def test_attention_wide_grid_sampled_rows(case):
 
 def _shape_cases():
     """Shapes that land in each launch regime for this device's CU count: 8-wave workgroups with
-    the keys split in two (at most one 128-row block per CU and at least 512 keys), 4-wave
-    workgroups (short key loops, or between one and four 128-row blocks per CU)."""
+    the keys split in two (at most one 128-row block per CU and at least 512 keys) or in four
+    (d = 64, at least 1024 keys, no band), 4-wave workgroups (short key loops, or between one and
+    four 128-row blocks per CU)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks4 = (3 * cus) // 2          # 128-row blocks: 1.5 per CU -> 4-wave workgroups
     H4 = 64
@@ -180,10 +181,16 @@ def _shape_cases():
         ("wave4_bf16_d128", 1, Lq4, 900, H4, 16, 128, "bf16", False, None),
         ("wave4_causal_f16_d64", 1, Lq4, Lq4, H4, H4, 64, "f16", True, None),
         ("wave4_window_bf16_d128", 1, Lq4, Lq4 + 50, H4, 8, 128, "bf16", False, (200, 0)),
+        # d = 64, rows over >= 1024 keys: four key groups over 64-row blocks (causal, or few blocks),
+        # ragged key tails, groups stepping past the block's last tile; a band keeps two groups
+        ("split4_causal_f16_d64", 2, 1000, 1100, 3, 3, 64, "f16", True, None),
+        ("split4_ragged_gqa_bf16_d64", 1, 333, 1500, 4, 2, 64, "bf16", False, None),
+        ("split4_causal_odd_bf16_d64", 1, 1090, 1090, 2, 1, 64, "bf16", True, None),
+        ("split_window_f16_d64", 1, 1100, 1100, 2, 2, 64, "f16", False, (256, 0)),
     ]
 
 
-@pytest.mark.parametrize("idx", range(8))
+@pytest.mark.parametrize("idx", range(12))
 def test_launch_regimes_sampled_rows(idx):
     name, B, Lq, Lk, Hq, Hkv, d, dtype, causal, window = _shape_cases()[idx]
     print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} window={window}",

@@ -49,6 +49,7 @@ CASES = [
     ("bf16_probs_long", 1, 300, 4100, 4, 4, 128, "bf16", (-1, -1), False, False),
     ("balanced_stream", 1, 1785, 7140, 40, 40, 128, "bf16", (-1, -1), True, False),
     ("causal_f16_d64", 2, 700, 700, 8, 8, 64, "f16", (-1, 0), False, False),
+    ("four_groups_causal_f16_d64", 2, 1000, 1100, 3, 3, 64, "f16", (-1, 0), False, False),
     ("window_bf16", 1, 900, 1000, 4, 2, 128, "bf16", (200, 30), False, False),
     ("fp8", 1, 333, 1200, 4, 2, 128, "e4m3", (-1, -1), False, False),
     ("fp8_probs", 1, 333, 1200, 4, 2, 128, "e4m3p", (-1, 0), False, False),
