@@ -95,6 +95,9 @@ struct KParams {
     // query row i's angles), pairing 1 split (r, r + D/2) or 2 interleaved (2r, 2r + 1).
     const float* q_cs;
     int q_rope;
+    // Four key groups only: 1 = each workgroup takes the pair of query blocks (i, n_qblk - 1 - i)
+    // of one (batch, head), its key groups divided between the two (causal rows, no left edge).
+    int pair;
 };
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
@@ -251,6 +254,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     constexpr int kOArea = 32 * OST;   // elements per row wave
     constexpr bool kLdsOut = !FP8 && (kRW / 2) * kOArea * 2 <= (int)sizeof(Ks) &&
                              (kRW - kRW / 2) * kOArea * 2 <= (int)sizeof(Vs);
+    // (with paired blocks the lead of block B uses its own group's buffers)
+    static_assert(KS != 4 || !kLdsOut || ((kRW / 2) * kOArea * 2 <= (int)sizeof(Ks) / KS &&
+                                          (kRW - kRW / 2) * kOArea * 2 <= (int)sizeof(Vs) / KS),
+                  "an output area must fit one group's tile buffers");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -274,10 +281,36 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // the unnormalised partial result there instead of the output.
     auto unit = [&](int ubid, int seg_ta, int seg_tb, int part_slot) __attribute__((always_inline)) {
     int qblk = ubid % p.n_qblk;
-    const int bh = ubid / p.n_qblk;
+    int bh = ubid / p.n_qblk;
+    if (p.win_right >= 0) qblk = p.n_qblk - 1 - qblk;  // causal-like bands: longest rows first
+    // Paired blocks (four key groups, causal rows with no left edge): blocks A = i and
+    // B = n_qblk - 1 - i see nA + nB = about n_qblk + 1 key tiles together; groups [0, kA) take A
+    // and [kA, 4) take B, kA chosen so that the longer of the two groups' runs is shortest. Every
+    // group runs S steps (they share the barriers); steps past a group's own run are dead.
+    const bool paired = KS == 4 && p.pair;
+    int kA = KS, pS = 0;  // groups on block A; steps of every group
+    if (paired) {
+        const int npair = (p.n_qblk + 1) / 2;
+        const int pi = ubid % npair;
+        bh = ubid / npair;
+        const int blkB = p.n_qblk - 1 - pi;
+        auto tiles = [&](int blk) __attribute__((always_inline)) {
+            const int last = min(blk * kBM + kBM, p.Lq) - 1;
+            return (min(p.Lk, last + (p.Lk - p.Lq) + p.win_right + 1) + kBN - 1) / kBN;
+        };
+        const int nA = tiles(pi), nB = blkB != pi ? tiles(blkB) : 0;
+        pS = (nA + KS - 1) / KS;
+        if (nB > 0) {
+            pS = 1 << 30;
+            for (int k = 1; k < KS; ++k) {
+                const int sk = max((nA + k - 1) / k, (nB + KS - k - 1) / (KS - k));
+                if (sk < pS) { pS = sk; kA = k; }
+            }
+        }
+        qblk = ks < kA ? pi : blkB;
+    }
     const int h = bh % p.Hq;
     const int b = bh / p.Hq;
-    if (p.win_right >= 0) qblk = p.n_qblk - 1 - qblk;  // causal-like bands: longest rows first
     const int hk = h / p.group;
 
     const int qb0 = qblk * kBM;
@@ -300,9 +333,18 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // Key groups split [t0, nkt) into consecutive runs of nsteps tiles; every group runs the same
     // number of steps (they share the barriers), so the last group may step over tiles >= nkt:
     // those re-read the last tile and are masked out entirely (tr <= nkt).
-    const int nsteps = KS == 1 ? nkt - t0 : (nkt - t0 + KS - 1) / KS;
-    const int ta = t0 + ks * nsteps;
-    const int tend = KS == 1 ? nkt : ta + nsteps;
+    int nsteps = KS == 1 ? nkt - t0 : (nkt - t0 + KS - 1) / KS;
+    int ta = t0 + ks * nsteps;
+    int tend = KS == 1 ? nkt : ta + nsteps;
+    int tv = tend;  // end of this group's own tiles
+    if (paired) {  // this group's share of its block, then dead steps up to the common count
+        const int ngrp = ks < kA ? kA : KS - kA, jg = ks < kA ? ks : ks - kA;
+        nsteps = (nkt - t0 + ngrp - 1) / ngrp;
+        ta = t0 + jg * nsteps;
+        tv = ta + nsteps;
+        tend = ta + pS;
+        tr = min(tr, tv);
+    }
     // this lane's visible keys [key_lo, key_lo + key_span] (rows past Lq may get an empty or
     // wrapped range; their scores are never stored)
     int key_lo, key_hi;
@@ -310,13 +352,15 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         const int64_t pos = (int64_t)qrow + shift;
         key_lo = p.win_left >= 0 ? (int)max64(0, pos - p.win_left) : 0;
         key_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, pos + p.win_right) : p.Lk - 1;
+        if (paired) key_hi = min(key_hi, tv * kBN - 1);
     }
     const unsigned key_span = (unsigned)(key_hi - key_lo);
     // keys some row of this wave can see, [wave_lo, wave_hi] (rows past Lq only widen it): an
     // edge tile outside it is skipped by this wave (its MFMAs, softmax and P*V), while the wave
     // still stages tiles and meets every barrier
     const int wave_lo = p.win_left >= 0 ? (int)max64(0, (int64_t)r0 + shift - p.win_left) : 0;
-    const int wave_hi = p.win_right >= 0 ? (int)min64(p.Lk - 1, (int64_t)r0 + 31 + shift + p.win_right) : p.Lk - 1;
+    const int wave_hi = min(p.win_right >= 0 ? (int)min64(p.Lk - 1, (int64_t)r0 + 31 + shift + p.win_right) : p.Lk - 1,
+                            paired ? tv * kBN - 1 : 0x7fffffff);
     auto dead_tile = [&](int tt) __attribute__((always_inline)) { return tt * kBN > wave_hi || tt * kBN + kBN - 1 < wave_lo; };
     // Balanced launches have no windows or causal masks (only key tails), so no tile is dead
     // there; their kernel, at its register limit, keeps the plain sequence of steps.
@@ -775,11 +819,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         }
     }
 
+    // the group that merges and stores this group's block: group 0, or kA for block B of a pair
+    const int lead = paired && ks >= kA ? kA : 0;
     if constexpr (KS > 1) {
         // Merge the key groups' partial results through LDS (the tiles are no longer read: every
         // step ended with a barrier): (m, l, O) = (max_i m_i, sum_i l_i a_i, sum_i O_i a_i) with
-        // a_i = exp2(m_i - m). Groups 1 .. KS-1 hand over m and l through the K buffers and O
-        // through the V buffers, DBR 32-feature blocks per round; group 0 merges and stores.
+        // a_i = exp2(m_i - m). The other groups of a block hand over m and l through the K
+        // buffers and O through the V buffers, DBR 32-feature blocks per round; the block's lead
+        // group merges and stores.
         constexpr int kOut = KS - 1;           // groups that hand over
         constexpr int kPerDb = kRW * 16 * 64;  // floats of one 32-feature block, all row waves of a group
         constexpr int kFit = (int)(sizeof(Vs) / 4 / (kPerDb * kOut));
@@ -789,25 +836,30 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
         float* const area_base = reinterpret_cast<float*>(&Vs[0][0]) + rw * (DBR * 16 * 64) + lane;
         auto ml = [&](int g) __attribute__((always_inline)) { return ml_base + (g - 1) * kRW * 128; };
         auto area = [&](int g) __attribute__((always_inline)) { return area_base + (g - 1) * kRW * (DBR * 16 * 64); };
+        // Group gg hands its result to this wave's lead (uniform over the wave). Every group but
+        // 0 writes its slot (block B's lead too), so a lead reads finite values from every slot
+        // and weights the other block's groups by exp2(-inf) = 0, without branches.
+        const int lead_end = paired && ks < kA ? kA : KS;
+        auto member = [&](int gg) __attribute__((always_inline)) { return gg > lead && gg < lead_end; };
         if (ks > 0) {
             ml(ks)[0] = m_run;
             ml(ks)[64] = l_run;
         }
         __syncthreads();
         float a0 = 1.f, ag[kOut];
-        if (ks == 0) {
+        if (ks == lead) {
             float mg[kOut], mn = m_run;
 #pragma unroll
-            for (int g = 1; g < KS; ++g) {
-                mg[g - 1] = ml(g)[0];
-                mn = fmaxf(mn, mg[g - 1]);
+            for (int gg = 1; gg < KS; ++gg) {
+                mg[gg - 1] = member(gg) ? ml(gg)[0] : -INFINITY;
+                mn = fmaxf(mn, mg[gg - 1]);
             }
             a0 = __builtin_amdgcn_exp2f(m_run - mn);
             l_run *= a0;
 #pragma unroll
-            for (int g = 1; g < KS; ++g) {
-                ag[g - 1] = __builtin_amdgcn_exp2f(mg[g - 1] - mn);
-                l_run += ml(g)[64] * ag[g - 1];
+            for (int gg = 1; gg < KS; ++gg) {
+                ag[gg - 1] = __builtin_amdgcn_exp2f(mg[gg - 1] - mn);
+                l_run += ml(gg)[64] * ag[gg - 1];
             }
         }
 #pragma unroll
@@ -820,14 +872,14 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                     for (int r = 0; r < 16; ++r) mine[((db - d0) * 16 + r) * 64] = o[db][r];
             }
             __syncthreads();
-            if (ks == 0) {
+            if (ks == lead) {
 #pragma unroll
                 for (int db = d0; db < d0 + DBR && db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float acc = o[db][r] * a0;
 #pragma unroll
-                        for (int g = 1; g < KS; ++g) acc += area(g)[((db - d0) * 16 + r) * 64] * ag[g - 1];
+                        for (int gg = 1; gg < KS; ++gg) acc += area(gg)[((db - d0) * 16 + r) * 64] * ag[gg - 1];
                         o[db][r] = acc;
                     }
             }
@@ -835,7 +887,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             // pass through the same buffers
             if (d0 + DBR < DB || kLdsOut) __syncthreads();
         }
-        if (ks > 0) return;
+        if (ks != lead) return;
     }
 
     if constexpr (SK) {
@@ -879,8 +931,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // that touch 32 rows each; the whole-row stores need 8x fewer cache-line requests, which
     // matters when every workgroup of a round stores at once (short key loops).
     if constexpr (kLdsOut) {
-        uint16_t* const area = rw < kRW / 2 ? reinterpret_cast<uint16_t*>(&Ks[0][0]) + rw * kOArea
-                                            : &Vs[0][0] + (rw - kRW / 2) * kOArea;
+        // (the lead group's own tile buffers: the two leads of a pair store at the same time)
+        uint16_t* const area = rw < kRW / 2 ? reinterpret_cast<uint16_t*>(&Ks[lead][0]) + rw * kOArea
+                                            : &Vs[lead][0] + (rw - kRW / 2) * kOArea;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1110,8 +1163,12 @@ KParams make_params(const AttnArgs& a) {
 }
 
 template <int D, int DT, int NW, int KS, bool BIG = false>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-    const KParams p = make_params<D, DT, NW, KS>(a);
+hipError_t launch(const AttnArgs& a, hipStream_t stream, bool paired = false) {
+    KParams p = make_params<D, DT, NW, KS>(a);
+    if (paired) {  // one workgroup per pair of 64-row blocks (four key groups)
+        p.pair = 1;
+        p.nblocks = (int)((int64_t)((p.n_qblk + 1) / 2) * a.Hq * a.B);
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<D, DT, NW, KS, false, BIG>), dim3((unsigned)p.nblocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
@@ -1183,9 +1240,15 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
         // against the two-group shape: causal [2,1024,8,64] +20 %, [1,4096,8,64] +13 %,
         // [2,2048,8,64] +2 %, non-causal [1,2048,4,64] +26 %; a (256, 0) window over the same
         // grid -64 %, so banded rows keep two groups.
+        // Causal blocks that would need a second round of such workgroups are paired instead
+        // (block i with block n - 1 - i, one round, the groups divided between the two).
         if constexpr (D == 64)
-            if (a.win_left < 0 && a.Lk >= 1024 && (a.win_right >= 0 || 2 * wg128 <= cus))
-                return launch<D, DT, 8, 4>(a, stream);
+            if (a.win_left < 0 && a.Lk >= 1024 && (a.win_right >= 0 || 2 * wg128 <= cus)) {
+                const int64_t nq64 = (a.Lq + 63) / 64;
+                const bool pair = a.win_right >= 0 && nq64 * a.Hq * a.B > cus &&
+                                  (nq64 + 1) / 2 * a.Hq * a.B <= cus;
+                return launch<D, DT, 8, 4>(a, stream, pair);
+            }
         return launch<D, DT, 8, 2>(a, stream);
     }
     return launch<D, DT, 4, 1>(a, stream);

@@ -165,7 +165,8 @@ def test_attention_wide_grid_sampled_rows(case):
 def _shape_cases():
     """Shapes that land in each launch regime for this device's CU count: 8-wave workgroups with
     the keys split in two (at most one 128-row block per CU and at least 512 keys) or in four
-    (d = 64, at least 1024 keys, no band), 4-wave workgroups (short key loops, or between one and
+    (d = 64, at least 1024 keys, no band; causal blocks paired when they would take two rounds),
+    4-wave workgroups (short key loops, or between one and
     four 128-row blocks per CU)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks4 = (3 * cus) // 2          # 128-row blocks: 1.5 per CU -> 4-wave workgroups
@@ -187,10 +188,13 @@ def _shape_cases():
         ("split4_ragged_gqa_bf16_d64", 1, 333, 1500, 4, 2, 64, "bf16", False, None),
         ("split4_causal_odd_bf16_d64", 1, 1090, 1090, 2, 1, 64, "bf16", True, None),
         ("split_window_f16_d64", 1, 1100, 1100, 2, 2, 64, "f16", False, (256, 0)),
+        # causal 64-row blocks that would need two rounds: paired blocks (i, n - 1 - i), an odd
+        # block count (the middle block alone), ragged last block, bottom-right causal offset
+        ("pair4_causal_odd_bf16_d64", 1, 33 * 64 - 21, 33 * 64 + 19, cus // 17, cus // 17, 64, "bf16", True, None),
     ]
 
 
-@pytest.mark.parametrize("idx", range(12))
+@pytest.mark.parametrize("idx", range(13))
 def test_launch_regimes_sampled_rows(idx):
     name, B, Lq, Lk, Hq, Hkv, d, dtype, causal, window = _shape_cases()[idx]
     print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} window={window}",

@@ -50,6 +50,7 @@ CASES = [
     ("balanced_stream", 1, 1785, 7140, 40, 40, 128, "bf16", (-1, -1), True, False),
     ("causal_f16_d64", 2, 700, 700, 8, 8, 64, "f16", (-1, 0), False, False),
     ("four_groups_causal_f16_d64", 2, 1000, 1100, 3, 3, 64, "f16", (-1, 0), False, False),
+    ("paired_blocks_causal_bf16_d64", 1, 2091, 2131, 15, 15, 64, "bf16", (-1, 0), False, False),
     ("window_bf16", 1, 900, 1000, 4, 2, 128, "bf16", (200, 30), False, False),
     ("fp8", 1, 333, 1200, 4, 2, 128, "e4m3", (-1, -1), False, False),
     ("fp8_probs", 1, 333, 1200, 4, 2, 128, "e4m3p", (-1, 0), False, False),
