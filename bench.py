@@ -241,9 +241,10 @@ def make_workload(name: str, dev: str, use_ws: bool = True):
         binding.qk_norm_rope(q, qb, k, cache.k[:, slot:], gq_in if inner else gq, gk_in if inner else gk, q_ang,
                              1e-6, scope, binding.SA_ROPE_SPLIT | flag, k_out_bstride=S * w.Hkv * w.d)
 
-    def append():
-        (_, _, v), _, slot = next_set()
-        binding.kv_cache_append(None, v, None, cache.v, slot // Lc, 0, S)
+    def append():  # sources rotate over all 30 chunk-sized input tensors (550 MB), not just the Vs
+        i = rot["i"]
+        rot["i"] = i + 1
+        binding.kv_cache_append(None, sets[(i // 3) % nsets][i % 3], None, cache.v, i % nslots, 0, S)
 
     def prologue_v():  # the one-launch prologue: queries, keys and values
         (q, k, v), qb, slot = next_set()
