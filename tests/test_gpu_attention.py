@@ -191,10 +191,12 @@ def _shape_cases():
         # causal 64-row blocks that would need two rounds: paired blocks (i, n - 1 - i), an odd
         # block count (the middle block alone), ragged last block, bottom-right causal offset
         ("pair4_causal_odd_bf16_d64", 1, 33 * 64 - 21, 33 * 64 + 19, cus // 17, cus // 17, 64, "bf16", True, None),
+        # paired blocks with a batch of two and grouped K/V heads (4 query heads per K/V head)
+        ("pair4_causal_gqa_batch_f16_d64", 2, 18 * 64 - 30, 18 * 64 - 30, cus // 32, cus // 128, 64, "f16", True, None),
     ]
 
 
-@pytest.mark.parametrize("idx", range(13))
+@pytest.mark.parametrize("idx", range(14))
 def test_launch_regimes_sampled_rows(idx):
     name, B, Lq, Lk, Hq, Hkv, d, dtype, causal, window = _shape_cases()[idx]
     print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} window={window}",
