@@ -286,7 +286,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     // Paired blocks (four key groups, causal rows with no left edge): blocks A = i and
     // B = n_qblk - 1 - i see nA + nB = about n_qblk + 1 key tiles together; groups [0, kA) take A
     // and [kA, 4) take B, kA chosen so that the longer of the two groups' runs is shortest. Every
-    // group runs S steps (they share the barriers); steps past a group's own run are dead.
+    // group runs S steps (they share the barriers); steps past a group's own run are dead. Both
+    // blocks have at least one key tile (the entry points require Lq <= Lk + right, so every
+    // query sees a key), so the step loop below runs for the groups of both blocks.
     const bool paired = KS == 4 && p.pair;
     int kA = KS, pS = 0;  // groups on block A; steps of every group
     if (paired) {

@@ -312,8 +312,8 @@ int64_t attn_forward_workspace_bytes(int d);
  * the same number of whole query blocks, then an equal piece of the key tiles of the remaining
  * blocks; each piece hands over its partial (O, row maximum, row sum) through the workspace, and
  * a second kernel merges the pieces of each split block in key order (deterministic, no
- * atomics). Only for full-range (no causal, no window) attention whose key loop has at least 32
- * tiles of 64 keys (Lk > 1984); other calls take the plain launch. Whole query blocks are
+ * atomics). Only for full-range (no causal, no window) attention whose key loop has at least 16
+ * tiles of 64 keys (Lk > 960); other calls take the plain launch. Whole query blocks are
  * computed exactly as by the 8-wave plain launch; split ones equal it up to the rounding of the
  * merge (within the same bounds). Calls that overlap on one workspace race.
  */
