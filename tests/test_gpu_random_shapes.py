@@ -127,3 +127,56 @@ def test_random_fp8_and_fused_query_norm_match_oracle(case):
         ref = oracle.attention(qs, K, V, scale, rows=rows)
     torch.cuda.synchronize()
     assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name, ulp_floor=True)
+
+
+def _key_group_cases():
+    """d = 64 shapes drawn from a fixed seed and kept when they land in the four-key-group launch
+    regimes for this device's CU count (the host-side launch rules, restated): four groups over
+    64-row blocks dispatched longest first, and causal blocks paired (i, n - 1 - i) in one round.
+    Ragged query and key lengths, grouped K/V heads, batches of one and two, both 16-bit types."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.RandomState(4242)
+    want = {"paired": 4, "four": 4}
+    out = []
+    for _ in range(20000):
+        if not any(want.values()):
+            break
+        B = int(rng.choice([1, 2]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        Lq = int(rng.randint(1024, 4200))
+        causal = bool(rng.randint(4))  # mostly causal
+        Lk = int(rng.randint(max(Lq, 1024), Lq + 300)) if causal else int(rng.randint(1024, 4200))
+        wg128 = -(-Lq // 128) * Hq * B
+        nq64 = -(-Lq // 64)
+        if not (wg128 <= cus and (causal or 2 * wg128 <= cus)):
+            continue
+        kind = "paired" if causal and nq64 * Hq * B > cus and (nq64 + 1) // 2 * Hq * B <= cus else "four"
+        if want[kind] == 0:
+            continue
+        want[kind] -= 1
+        dtype = str(rng.choice(["bf16", "f16"]))
+        out.append((f"{kind}{len(out)}", B, Lq, Lk, Hq, Hkv, 64, dtype, causal))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_random_key_group_regimes_match_oracle(idx):
+    """Seeded d = 64 shapes in the four-key-group regimes (plain and paired causal blocks): a row
+    sample covering every 64-row block against the oracle. (The cases depend on the device's CU
+    count, so they are drawn when the test runs.)"""
+    case = _key_group_cases()[idx]
+    name, B, Lq, Lk, Hq, Hkv, d, dtype, causal = case
+    print(f"[case] {case}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=5200 + Lq % 991)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty_like(qd)
+    (binding.attn_forward if dtype == "bf16" else binding.attn_forward_f16)(qd, kd, vd, out, d ** -0.5, causal)
+    torch.cuda.synchronize()
+    # every block's first and last row of every (batch, head), plus a random sample
+    edge = np.array([(b * Lq + t) * Hq + h for b in range(B) for h in range(Hq)
+                     for blk in range(-(-Lq // 64)) for t in (64 * blk, min(Lq, 64 * blk + 64) - 1)], dtype=np.int64)
+    rows = np.union1d(edge, sample_rows(B, Lq, Hq, 1024, seed=Lq + Lk))
+    Q, K, V = (widen(x).reshape(x.shape) for x in (q, k, v))
+    ref = oracle.attention(Q, K, V, d ** -0.5, causal=causal, rows=rows)
+    assert_attention_close(out.reshape(-1, d)[torch.from_numpy(rows).to(DEV)], ref, name, ulp_floor=True)
