@@ -1108,6 +1108,8 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kScratchMaxDevices = 64;
 
 constexpr int kBalancedMinTiles = 16;
+// Key loops (64-key tiles) from which grids far smaller than the CUs split them (launch_shape).
+constexpr int kSplitMinTiles = 32;
 
 // A balanced launch pays when the grid's rounds would keep the slots under 90 % busy, for
 // full-range attention (every unit the same number of key tiles), more units than slots and key
@@ -1218,6 +1220,21 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     const int tiles8 = (a.Lk + kTileKeys - 1) / kTileKeys;
     if (a.ws && a.ws_bytes >= balanced_workspace_bytes(a.d, (int)cus) && balanced_pays(a, wg256, cus, tiles8))
         return launch_balanced<D, DT>(a, (int)cus, stream);
+    // Grids of at most a quarter as many 128-row blocks as CUs over long key loops (a few query
+    // rows per head over a long context) are set by the loop's serial steps, not by the CUs: with
+    // a workspace and full-range rows, every 256-row unit's key tiles are cut into equal pieces,
+    // one persistent workgroup each (up to one per CU), and the merge kernel combines them.
+    // Measured on MI355X against the plain launch (d = 128, two key groups there): 16 heads x 64
+    // queries over 4096 keys (64 tiles) 2.35x faster, over 3072 keys 2.0x; 8 x 1024 queries over
+    // 2048 keys (32 tiles) 1.34x, 8 x 256 queries 1.13x; one query row per head over 8192 keys
+    // 1.6x; shorter loops lose (16 tiles -5 %, 8 x 257 over 257 keys -32 %: the second launch
+    // and the merge outweigh the steps saved). At d = 64 the four key groups of one workgroup
+    // are faster (the split: -13 % to -32 %).
+    const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
+    if (D == 128 && a.ws && a.win_left < 0 && a.win_right < 0 && wg128 * 4 <= cus && tiles8 >= kSplitMinTiles) {
+        const int wgs = (int)std::min<int64_t>(cus, wg256 * tiles8);
+        if (a.ws_bytes >= balanced_workspace_bytes(a.d, wgs)) return launch_balanced<D, DT>(a, wgs, stream);
+    }
     // Banded rows -- a window of at most 2048 + 1 keys, or causal rows of at most 4096 keys --
     // waste less on edge tiles in 128-row blocks, which halves the keys a block visits beyond
     // its rows' bands. Measured on MI355X with two or more 256-row blocks per CU: window (256, 0)
@@ -1232,7 +1249,6 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
     // 128-row slots) and loops of 512-1024 keys 9 %, so those keep 128-row blocks.
     const bool full8 = wg256 >= cus && wg256 * 10 >= (wg256 + cus - 1) / cus * cus * 9;
     if (wg256 >= 4 * cus || (full8 && a.Lk >= 2048)) return launch<D, DT, 8, 1>(a, stream);
-    const int64_t wg128 = (int64_t)((a.Lq + 127) / 128) * a.Hq * a.B;
     if (wg128 <= cus && a.Lk >= 512) {
         // d = 64, rows over at least 1024 keys with no left window edge: four key groups over
         // 64-row blocks (twice the blocks, each group a quarter of the loop) when causal rows

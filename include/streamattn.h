@@ -315,7 +315,10 @@ int64_t attn_forward_workspace_bytes(int d);
  * atomics). Only for full-range (no causal, no window) attention whose key loop has at least 16
  * tiles of 64 keys (Lk > 960); other calls take the plain launch. Whole query blocks are
  * computed exactly as by the 8-wave plain launch; split ones equal it up to the rounding of the
- * merge (within the same bounds). Calls that overlap on one workspace race.
+ * merge (within the same bounds). At d = 128, grids with at most a quarter as many 128-row query
+ * blocks as CUs over key loops of at least 32 tiles (Lk > 1984; few query rows over a long
+ * context) split every block's key tiles the same way, into equal pieces on up to one
+ * workgroup per CU. Calls that overlap on one workspace race.
  */
 int attn_forward_ws(const void* q, const void* k, const void* v, void* out,
                     int B, int Hq, int Hkv, int Lq, int Lk, int d,

@@ -108,3 +108,43 @@ def test_balanced_whole_blocks_bit_exact_repeatable_and_small_workspace_falls_ba
     ri = torch.from_numpy(rows).to(DEV)
     assert_attention_close(a.reshape(-1, d)[ri], ref, "balanced")
     assert_attention_close(c.reshape(-1, d)[ri], ref, "fallback")
+
+
+def _split_cases():
+    cus = _cus()
+    q_rows = cus // 4 // 8 * 128  # 8 heads: exactly a quarter as many 128-row blocks as CUs
+    return [
+        # name, B, Lq, Lk, Hq, Hkv, d, dtype: d = 128 grids of at most cus / 4 128-row blocks
+        # over key loops of at least 32 tiles (64 keys), whose key tiles are split over the CUs
+        ("split_bf16_d128_64q", 1, 64, 4096, 16, 16, 128, "bf16"),
+        ("split_f16_gqa_ragged", 1, 100, 3000, 8, 2, 128, "f16"),
+        ("split_bf16_one_query_batch2", 2, 1, 2100, 16, 4, 128, "bf16"),
+        ("split_fp8_d128", 1, 64, 2500, 8, 8, 128, "e4m3"),
+        ("split_bf16_quarter_grid_32_tiles", 1, q_rows, 2048, 8, 8, 128, "bf16"),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_split_key_small_grid_matches_oracle(idx):
+    # every row against the oracle; the split changes the order in which a row's key tiles are
+    # summed, so the result differs from the plain launch's somewhere, while a workspace too
+    # small for the split takes the plain launch bit for bit
+    name, B, Lq, Lk, Hq, Hkv, d, dtype = _split_cases()[idx]
+    print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype}", flush=True)
+    q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=zlib.crc32(name.encode()) % 10000)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    odt = torch.float16 if dtype == "f16" else torch.bfloat16
+    out, small, plain = (torch.empty(q.shape, dtype=odt, device=DEV) for _ in range(3))
+    ws = binding.attn_workspace(d)
+    binding.attn_forward_ws(qd, kd, vd, out, d ** -0.5, ws)
+    binding.attn_forward_ws(qd, kd, vd, small, d ** -0.5, ws[:1024])
+    if dtype == "e4m3":
+        binding.attn_forward_fp8(qd, kd, vd, plain, d ** -0.5, False)
+    else:
+        binding.attn_forward_kvstride(qd, kd, vd, plain, Lk, d ** -0.5, False)
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), plain.view(torch.int16)), name
+    assert not torch.equal(out.view(torch.int16), plain.view(torch.int16)), name
+    Q, K, V = (widen(x).reshape(x.shape) for x in (q, k, v))
+    ref = oracle.attention(Q, K, V, d ** -0.5)
+    assert_attention_close(out.reshape(-1, d), ref.reshape(-1, d), name)
