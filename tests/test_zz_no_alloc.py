@@ -65,3 +65,26 @@ def test_static_scratch_rejects_bad_arguments_before_launch():
     with pytest.raises(binding.StreamAttnError) as e:
         binding.attn_forward_ws_static(q, q, q, torch.empty_like(q), 0.1)
     assert e.value.status == binding.SA_ERR_UNSUPPORTED_CODE
+
+
+def test_static_scratch_split_key_small_grid_on_two_calls():
+    # the split key loops of small d = 128 grids (few query rows over 32+ key tiles) through the
+    # allocation-free entry point: bit for bit as with a caller workspace, every row against the
+    # oracle, the second call on a smaller input
+    cases = [("static_split_64q_4096k", 1, 64, 4096, 16, 16, 128, "bf16"),
+             ("static_split_one_query_smaller", 2, 1, 2100, 16, 4, 128, "bf16")]
+    sizes = []
+    for i, (name, B, Lq, Lk, Hq, Hkv, d, dtype) in enumerate(cases):
+        print(f"[case] {name} B={B} Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} {dtype}", flush=True)
+        q, k, v = synthetic.attention_inputs(B, Lq, Lk, Hq, Hkv, d, dtype, seed=4300 + i)
+        sizes.append(q.numel() + k.numel())
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        out_static = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        out_ws = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        binding.attn_forward_ws_static(qd, kd, vd, out_static, d ** -0.5)
+        binding.attn_forward_ws(qd, kd, vd, out_ws, d ** -0.5, binding.attn_workspace(d))
+        torch.cuda.synchronize()
+        assert torch.equal(out_static.view(torch.int16), out_ws.view(torch.int16)), name
+        Q, K, V = (widen(x).reshape(x.shape) for x in (q, k, v))
+        assert_attention_close(out_static.reshape(-1, d), oracle.attention(Q, K, V, d ** -0.5).reshape(-1, d), name)
+    assert sizes[1] < sizes[0]
