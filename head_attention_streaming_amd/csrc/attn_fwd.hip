@@ -5,7 +5,8 @@
 // exact tiled attention with an online softmax (the IO-aware tiling the FlashAttention papers
 // describe, which the "optimizing-attention-flash" page cites): keys are streamed in tiles, a
 // running row maximum m and row sum l are kept in registers, and the partial output is
-// rescaled by exp2(m_old - m_new) whenever the maximum grows. No score matrix is stored.
+// rescaled by exp2(m_old - m_new) when the maximum grows far enough past m to matter (m may lag
+// the true maximum; see the two checks at m's declaration). No score matrix is stored.
 //
 // Work decomposition (one workgroup = 128 or 256 query rows of one (batch, head)):
 //   * each wave owns 32 query rows; its Q^T slice stays in registers as the MFMA B operand;
@@ -561,14 +562,32 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                                       8 * (L16 & 1));
 
     const float c = p.c;
-    // Running maximum used as the exponent offset (log2 domain). It is raised only when a
-    // tile's maximum exceeds it by more than kRescaleSlack, so most tiles skip the O rescale;
-    // probabilities then stay below 2^kRescaleSlack, well inside f16 range. Finite start value,
-    // so exp2 never sees inf - inf.
+    // Exponent offset m (log2 domain), a running maximum of the scores that may lag the true one;
+    // a finite start value, so exp2 never sees inf - inf. Two ways to keep the lag safe:
+    //  * max check: each step takes the tile's maximum right after S = K Q^T and raises m only
+    //    when it exceeds m by more than kRescaleSlack (2^8 for 16-bit probabilities, so most
+    //    tiles skip the O rescale and probabilities stay below 2^8);
+    //  * sum check (kLazyMax): a tile's probabilities are computed against the current m, and
+    //    this lane's sum of them -- the row-sum term the kernel forms anyway -- checks the lag:
+    //    while every lane's sum is at most 2^15, every probability is at most 2^15 (inside f16
+    //    range; fp32 O and l stay far from overflow) and the tile needs no maximum at all;
+    //    otherwise (an f16 overflow shows as inf) the wave takes the tile's maximum, raises m to
+    //    it, rescales O and l and computes the probabilities again. The first tile always does;
+    //    later ones only when a tile's scores rise ~10 binades past m, so for such data m, and
+    //    every result, is the same as with the max check. It saves the per-step maximum (16
+    //    max3 of 32 scores, a lane swap, a ballot) and frees the score registers earlier.
+    //    Measured on MI355X against the max check (A/B in one process; the same bits where no
+    //    later tile rises 8+ binades past m): cross-attention 2 x 1785 x 512 keys -4 to -6 %
+    //    time, causal [1,4096,64,128] -8 %, window (1024, 0) [1,8192,16,128] -7.5 %, balanced
+    //    streaming attention -0.3 to -1.5 % (the 4-wave and balanced d = 128 kernels spill 9 and
+    //    11 registers instead of 23 and 17); the plain launch with bf16 probabilities +3.4 %,
+    //    FP8 +1.8 %, d = 64 windows and causal rows +2.6 to +4.7 %: those keep the max check.
     // P8 rounds the probabilities to E4M3 (largest 448), so it raises m with every new maximum and
     // offsets the exponent by 8: p = 2^(s c - m + 8) <= 2^8, normal down to 14 binades below m.
+    constexpr bool kLazyMax = D == 128 && !FP8 && !(PB && !SK);
     constexpr float kRescaleSlack = P8 ? 0.0f : 8.0f;
     constexpr float kPOff = P8 ? 8.0f : 0.0f;
+    constexpr float kSumLimit = 32768.0f;
     float m_run = -1e30f;
     float l_run = 0.f;  // this lane's share of the row sum (its own keys)
     f32x16 o[DB];
@@ -580,8 +599,34 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     u32x4 pf[KC];           // f16 probabilities of the previous tile (P^T operands)
     i32x8 pf8;              // P8: the previous tile's E4M3 probabilities (one 64-key P^T operand)
 
+    // the largest score of a (masked) tile for this lane's query row, in log2 units
+    auto tile_max = [&](const f32x16 (&sx)[KB]) __attribute__((always_inline)) {
+        float mk[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            mk[kb] = fmaxf(sx[kb][0], sx[kb][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) mk[kb] = fmaxf(fmaxf(mk[kb], sx[kb][r]), sx[kb][r + 1]);
+        }
+        float mloc = mk[0];
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb) mloc = fmaxf(mloc, mk[kb]);
+        return half_swap_max(mloc) * c;
+    };
+    // raise m to tmax (if larger) and rescale O and l to the new offset
+    auto rescale = [&](float tmax) __attribute__((always_inline)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    };
+
     // One pipeline step t:  S(t) = K(t) Q^T  ||  P(t-1) = exp2(S(t-1) c - m)  [MFMA || VALU]
-    //                       O += V(t-1) P(t-1)  ||  stage K(t+1), V(t); row max of S(t)
+    //                       O += V(t-1) P(t-1)  ||  stage K(t+1), V(t); masks (max check: row max) of S(t)
     // K(t) and V(t) live in LDS slot t%2; step t overwrites the slots step t-1 read, and the
     // barrier closing each step orders those writes before the next step's reads.
     auto step = [&](auto do_qk, auto do_pv, auto do_mask, int t, f32x16 (&sc)[KB], f32x16 (&sp)[KB]) __attribute__((always_inline)) {
@@ -665,35 +710,45 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
             l_run += acc0 + acc1;
         }
         if (!P8 && PV && !pv_dead) {
-            // P(t-1) as f16 operands; the row sum adds the f16 values the product uses
-            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-            float acc0 = 0.f, acc1 = 0.f;
+            // P(t-1) as f16 (bf16) operands; the row sum adds the rounded values the product uses
+            auto probs = [&]() __attribute__((always_inline)) {
+                const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+                float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int kb = kc >> 1, hh = kc & 1;
-                uint32_t w[4];
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int kb = kc >> 1, hh = kc & 1;
+                    uint32_t w[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e], c, -m_run));
-                    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e + 1], c, -m_run));
-                    if constexpr (PB) {
-                        w[e] = pack_bf16x2(x0, x1);
-                        const bf16x2 one_b = {(__bf16)1.0f, (__bf16)1.0f};
-                        if (e & 1)
-                            acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc1, false);
-                        else
-                            acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc0, false);
-                    } else {
-                        w[e] = pack_f16x2(x0, x1);
-                        if (e & 1)
-                            acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc1, false);
-                        else
-                            acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc0, false);
+                    for (int e = 0; e < 4; ++e) {
+                        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e], c, -m_run));
+                        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sp[kb][8 * hh + 2 * e + 1], c, -m_run));
+                        if constexpr (PB) {
+                            w[e] = pack_bf16x2(x0, x1);
+                            const bf16x2 one_b = {(__bf16)1.0f, (__bf16)1.0f};
+                            if (e & 1)
+                                acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc1, false);
+                            else
+                                acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one_b, acc0, false);
+                        } else {
+                            w[e] = pack_f16x2(x0, x1);
+                            if (e & 1)
+                                acc1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc1, false);
+                            else
+                                acc0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[e]), one2, acc0, false);
+                        }
                     }
+                    pf[kc] = u32x4{w[0], w[1], w[2], w[3]};
                 }
-                pf[kc] = u32x4{w[0], w[1], w[2], w[3]};
+                return acc0 + acc1;
+            };
+            float acc = probs();
+            if constexpr (kLazyMax) {
+                if (__builtin_amdgcn_ballot_w64(!(acc <= kSumLimit))) {  // m lags too far: raise it to the tile maximum
+                    rescale(tile_max(sp));
+                    acc = probs();
+                }
             }
-            l_run += acc0 + acc1;
+            l_run += acc;
         }
         if constexpr (QK) {
             if constexpr (kLdsCheck) __syncthreads();  // every wave has read K(t) from the one K slot
@@ -753,26 +808,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                         sc[kb][r] = rel <= key_span ? sc[kb][r] : -INFINITY;
                     }
             }
-            float mk[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                mk[kb] = fmaxf(sc[kb][0], sc[kb][1]);
-#pragma unroll
-                for (int r = 2; r < 16; r += 2) mk[kb] = fmaxf(fmaxf(mk[kb], sc[kb][r]), sc[kb][r + 1]);
-            }
-            float mloc = mk[0];
-#pragma unroll
-            for (int kb = 1; kb < KB; ++kb) mloc = fmaxf(mloc, mk[kb]);
-            const float tmax = half_swap_max(mloc) * c;
-            if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) {
-                const float m_new = fmaxf(m_run, tmax);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            if constexpr (!kLazyMax) {
+                const float tmax = tile_max(sc);
+                if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack)) rescale(tmax);
             }
         }
         __syncthreads();
