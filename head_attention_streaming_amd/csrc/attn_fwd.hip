@@ -580,11 +580,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
     //    later tile rises 8+ binades past m): cross-attention 2 x 1785 x 512 keys -4 to -6 %
     //    time, causal [1,4096,64,128] -8 %, window (1024, 0) [1,8192,16,128] -7.5 %, balanced
     //    streaming attention -0.3 to -1.5 % (the 4-wave and balanced d = 128 kernels spill 9 and
-    //    11 registers instead of 23 and 17); the plain launch with bf16 probabilities +3.4 %,
-    //    FP8 +1.8 %, d = 64 windows and causal rows +2.6 to +4.7 %: those keep the max check.
+    //    11 registers instead of 23 and 17), d = 64 8-wave launches of one key group -2.5 to
+    //    -2.8 %; the plain launch with bf16 probabilities +0.7 %, FP8 +1.8 %, the other d = 64
+    //    shapes (4-wave windows, four key groups) +2.8 to +4.4 %: those keep the max check.
     // P8 rounds the probabilities to E4M3 (largest 448), so it raises m with every new maximum and
     // offsets the exponent by 8: p = 2^(s c - m + 8) <= 2^8, normal down to 14 binades below m.
-    constexpr bool kLazyMax = D == 128 && !FP8 && !(PB && !SK);
+    constexpr bool kLazyMax = !FP8 && !(PB && !SK) && (D == 128 || (NW == 8 && KS == 1));
     constexpr float kRescaleSlack = P8 ? 0.0f : 8.0f;
     constexpr float kPOff = P8 ? 8.0f : 0.0f;
     constexpr float kSumLimit = 32768.0f;
@@ -741,12 +742,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_fwd_kernel(KParams p) {
                 }
                 return acc0 + acc1;
             };
-            float acc = probs();
+            float acc;
             if constexpr (kLazyMax) {
-                if (__builtin_amdgcn_ballot_w64(!(acc <= kSumLimit))) {  // m lags too far: raise it to the tile maximum
-                    rescale(tile_max(sp));
+                // at most two passes (one copy of the code): the second after raising m to the
+                // tile maximum when the first finds that m lags too far
+                for (int pass = 0;; ++pass) {
                     acc = probs();
+                    if (pass > 0 || !__builtin_amdgcn_ballot_w64(!(acc <= kSumLimit))) break;
+                    rescale(tile_max(sp));
                 }
+            } else {
+                acc = probs();
             }
             l_run += acc;
         }

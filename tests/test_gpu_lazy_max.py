@@ -1,6 +1,7 @@
-"""GPU parity of the exponent offset's sum check (the d = 128 16-bit kernels other than the plain
-bf16-probability launch): no per-tile maximum is taken, and a tile whose probability sum exceeds
-2^15 in some lane, or overflows f16, is recomputed after raising the offset to the tile maximum.
+"""GPU parity of the exponent offset's sum check (the 16-bit d = 128 kernels other than the plain
+bf16-probability launch, and the 8-wave one-key-group d = 64 ones): no per-tile maximum is taken,
+and a tile whose probability sum exceeds 2^15 in some lane, or overflows f16, is recomputed after
+raising the offset to the tile maximum.
 Each case plants keys late in the key loop that some query rows align with, so those rows' scores
 jump 15-50 binades past every earlier tile's (two jumps per row, in different tiles): the
 recompute path runs mid-loop, in balanced pieces and split loops as well. The planted rows and a
@@ -26,6 +27,7 @@ CASES = [
     ("plain_4wave_bf16_cross_shape", 2, 1785, 512, 40, 40, 128, "bf16", (-1, -1), True, (0.5, 0.9), (1.5, 3.0)),
     ("window_1024_bf16", 1, 4096, 4096, 8, 8, 128, "bf16", (1024, 0), False, (-0.6, -0.1), (1.5, 3.0)),
     ("split_small_grid_bf16_probs", 1, 64, 4096, 16, 16, 128, "bf16", (-1, -1), True, (0.5, 0.95), (1.5, 3.0)),
+    ("plain_8wave_d64_f16", 1, 8192, 8192, 16, 16, 64, "f16", (-1, -1), False, (0.3, 0.8), (2.0, 4.0)),
 ]
 
 
